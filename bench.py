@@ -1,0 +1,243 @@
+"""Benchmark of the low-bit all-reduce codec on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic operands:
+quantize the R operands (K1), dequantize-sum-requantize every hidden chunk
+(K2), dequantize the gathered result (K3) -- the quantize / Reduce-Scatter /
+requantize / All-Gather / dequantize sequence of "Flash Communication:
+Reducing Tensor Parallelization Bottleneck for Fast Large Language Model
+Inference" (Figure 5, right), with the two exchanges as HBM hand-offs.
+
+Workload: the LLaMA-3-70B prefill all-reduce of Figure 1 (batch 8 x 1024
+tokens, TP = 4): R=4 operands of T=8192 x H=8192 bf16, 4-bit codes, groups
+of 128. Inputs are seeded synthetic activations, resident in HBM before the
+timed region.
+
+Metric: algorithmic HBM bytes per step / time per step (GB/s). Algorithmic
+bytes: every input read once, each payload written once and read once, the
+output written once (scales and zeros 4 bytes per group).
+
+Prints one JSON line. `roofline` is for K1, the kernel that moves two thirds
+of the bytes, timed with HIP events on the stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of peak) for quant->dequant-sum-requant->dequant"
+WORKLOAD = "llama3_70b_prefill"
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_llama3_70b_prefill_traffic.txt")
+K1_SOURCES = ("bit_activation_compression_amd/csrc/fc_quantize.hip",
+              "bit_activation_compression_amd/csrc/fc_device.h")
+
+
+def model_bytes(R: int, T: int, H: int, bits: int, group: int, group2: int, e: int = 2) -> dict:
+    n1, n2 = R * T * H, T * H
+    p1 = n1 * bits // 8 + n1 // group * 4
+    p2 = n2 * bits // 8 + n2 // group2 * 4
+    k1 = n1 * e + p1
+    k2 = p1 + p2
+    k3 = p2 + n2 * e
+    return {"k1": k1, "k2": k2, "k3": k3, "total": k1 + k2 + k3, "payload1": p1, "payload2": p2}
+
+
+def k1_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in K1_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic() -> float | None:
+    """HBM bytes per K1 launch from the committed rocprofv3 counter summary, if it
+    was taken on the current K1 source; None otherwise."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    m_src = re.search(r"^k1_source_sha256_16:\s*(\S+)", txt, re.M)
+    m_b = re.search(r"^k1_hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    if not m_src or not m_b or m_src.group(1) != k1_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the CPU oracle (profiling runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this codec emulates the R ranks of one all-reduce on a single "
+                                   "GPU; runs on more than one GPU are not supported",
+                          "n_gpus": args.gpus}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    import bit_activation_compression_amd as fc
+    import synth
+
+    w = synth.workload(args.workload)
+    R, T, H, bits, group = w.R, w.T, w.H, w.bits, w.group
+    g2 = fc.fc_stage2_group(R, H, group)
+    mb = model_bytes(R, T, H, bits, group, g2)
+    tdt = torch.bfloat16 if w.dtype == synth.BF16 else torch.float16
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    print(f"[bench] generating {w.name}: R={R} T={T} H={H} {w.dtype} int{bits} g{group}",
+          file=sys.stderr, flush=True)
+    x_host = synth.operands(w, args.seed)
+
+    # Two buffer sets used in turn, so a step never finds the previous step's
+    # inputs or payloads in the caches.
+    sets = []
+    for _ in range(2):
+        xd = torch.from_numpy(x_host.view(np.int16)).to(dev).view(tdt)
+        c1 = torch.empty((R, T, H * bits // 8), dtype=torch.uint8, device=dev)
+        s1 = torch.empty((R, T, H // group), dtype=torch.uint16, device=dev)
+        z1 = torch.empty_like(s1)
+        c2 = torch.empty((T, H * bits // 8), dtype=torch.uint8, device=dev)
+        s2 = torch.empty((T, H // g2), dtype=torch.uint16, device=dev)
+        z2 = torch.empty_like(s2)
+        out = torch.empty((T, H), dtype=tdt, device=dev)
+        sets.append((xd, c1, s1, z1, c2, s2, z2, out))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i: int, ev=None) -> None:
+        xd, c1, s1, z1, c2, s2, z2, out = sets[i % 2]
+        if ev is not None:
+            ev[0].record(stream)
+        fc.fc_quantize_groups(xd, bits, group, c1, s1, z1, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fc.fc_dequant_sum_requant(c1, s1, z1, R, T, H, bits, group, c2, s2, z2, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        fc.fc_dequantize(c2, s2, z2, T, H, bits, g2, tdt, out, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    print(f"[bench] timing {K} steps after {args.warmup} warmup", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    k_ms = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(3)] for ev in events])
+    k_avg = k_ms.mean(axis=0)
+    k_med = np.median(k_ms, axis=0)
+    pipe_ms = np.array([ev[0].elapsed_time(ev[3]) for ev in events])
+
+    # a plain device-to-device copy of 1 GiB: the achievable streaming ceiling
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ce[0].record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    ce[1].record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) * 10 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
+    del src, dst
+
+    value = mb["total"] / (ms_per_step * 1e-3) / 1e9
+    k1_gbps = mb["k1"] / (k_avg[0] * 1e-3) / 1e9
+    traffic = measured_traffic()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        print("[bench] timing the CPU oracle on the full workload (1 thread)", file=sys.stderr,
+              flush=True)
+        c0 = time.perf_counter()
+        oracle.allreduce(x_host, w.dtype, bits, group, want_f32=False)
+        c_s = time.perf_counter() - c0
+        cpu = {"value": round(mb["total"] / c_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"the whole {w.name} workload (R={R}, T={T}, H={H}), one pass, single "
+                         f"thread, {c_s:.2f} s on {cpu_model()}"}
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "R": R, "T": T, "H": H, "io_dtype": w.dtype, "bits": bits,
+                   "group": group, "group2": g2, "dist": w.dist, "sigma": w.sigma,
+                   "outlier_channels": w.n_outliers, "outlier_scale": w.outlier_scale},
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "elements_per_s": round(R * T * H / (ms_per_step * 1e-3), 1),
+        "model_bytes": mb,
+        "kernel_ms_avg": {"k1_quantize": round(float(k_avg[0]), 5),
+                          "k2_dequant_sum_requant": round(float(k_avg[1]), 5),
+                          "k3_dequantize": round(float(k_avg[2]), 5)},
+        "kernel_ms_median": {"k1_quantize": round(float(k_med[0]), 5),
+                             "k2_dequant_sum_requant": round(float(k_med[1]), 5),
+                             "k3_dequantize": round(float(k_med[2]), 5)},
+        "kernel_gbps": {"k1_quantize": round(mb["k1"] / (k_avg[0] * 1e-3) / 1e9, 1),
+                        "k2_dequant_sum_requant": round(mb["k2"] / (k_avg[1] * 1e-3) / 1e9, 1),
+                        "k3_dequantize": round(mb["k3"] / (k_avg[2] * 1e-3) / 1e9, 1)},
+        "pipeline_ms_median_events": round(float(np.median(pipe_ms)), 5),
+        "copy_ceiling_gbps": round(copy_gbps, 1),
+        "roofline": {"bound": "hbm", "kernel": "k1_quantize", "achieved": round(k1_gbps, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(k1_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": mb["k1"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,199 @@
+"""Low-bit all-reduce activation codec for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in `include/fc.h` (libfc.so, built from
+`csrc/` by `build.py`). Every step of the codec runs in the library's HIP
+kernels; this module only checks tensor metadata, allocates outputs with
+torch on the input's device, and passes raw device pointers and the current
+HIP stream. There is no fallback: if the library cannot be loaded, calls
+raise.
+
+Method: "Flash Communication: Reducing Tensor Parallelization Bottleneck for
+Fast Large Language Model Inference" -- quantize the R partial sums before
+the Reduce-Scatter, reduce and requantize each hidden chunk before the
+All-Gather, dequantize after it (Figure 5, right; groups as in Figure 4).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "FcError", "lib", "library_path",
+    "fc_quantize_groups", "fc_dequant_sum_requant", "fc_dequantize", "fc_allreduce_emulated",
+    "fc_workspace_bytes", "fc_workspace_layout", "fc_stage2_group", "fc_status_string",
+    "workspace_views", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libfc.so")
+
+FC_F16, FC_BF16 = 0, 1
+_DTYPES = {torch.float16: FC_F16, torch.bfloat16: FC_BF16}
+EXPORTED_SYMBOLS = (
+    "fc_quantize_groups", "fc_dequant_sum_requant", "fc_dequantize", "fc_allreduce_emulated",
+    "fc_workspace_bytes", "fc_workspace_layout", "fc_stage2_group", "fc_status_string",
+)
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = lib().fc_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfc.so (building it with hipcc first if it is absent)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(library_path):
+                from . import build as _build
+                _build.build()
+            L = ctypes.CDLL(library_path)
+            P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+            L.fc_quantize_groups.argtypes = [P, I, I, I, I, I, I, P, P, P, P]
+            L.fc_dequant_sum_requant.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P]
+            L.fc_dequantize.argtypes = [P, P, P, I, I, I, I, I, P, P]
+            L.fc_allreduce_emulated.argtypes = [P, I, I, I, I, I, I, P, P, Z, P]
+            for f in (L.fc_quantize_groups, L.fc_dequant_sum_requant, L.fc_dequantize,
+                      L.fc_allreduce_emulated):
+                f.restype = I
+            L.fc_workspace_bytes.argtypes = [I, I, I, I, I]
+            L.fc_workspace_bytes.restype = Z
+            L.fc_workspace_layout.argtypes = [I, I, I, I, I, ctypes.POINTER(Z), ctypes.POINTER(Z)]
+            L.fc_workspace_layout.restype = I
+            L.fc_stage2_group.argtypes = [I, I, I]
+            L.fc_stage2_group.restype = I
+            L.fc_status_string.argtypes = [I]
+            L.fc_status_string.restype = ctypes.c_char_p
+            _lib = L
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise FcError(status, where)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_tensor(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fc_status_string(status: int) -> str:
+    return lib().fc_status_string(status).decode()
+
+
+def fc_stage2_group(R: int, H: int, group: int) -> int:
+    return lib().fc_stage2_group(R, H, group)
+
+
+def fc_workspace_bytes(R: int, T: int, H: int, bits: int, group: int) -> int:
+    return lib().fc_workspace_bytes(R, T, H, bits, group)
+
+
+def fc_workspace_layout(R: int, T: int, H: int, bits: int, group: int):
+    """[(offset, size)] of the six workspace slices: codes1, s1, z1, codes2, s2, z2."""
+    off = (ctypes.c_size_t * 6)()
+    size = (ctypes.c_size_t * 6)()
+    _check(lib().fc_workspace_layout(R, T, H, bits, group, off, size), "fc_workspace_layout")
+    return [(off[i], size[i]) for i in range(6)]
+
+
+def fc_quantize_groups(x: torch.Tensor, bits: int, group: int, codes1=None, s1=None, z1=None,
+                       stream=None):
+    """x [R, T, H] fp16/bf16 -> (codes1 [R, T, H*bits/8] u8, s1, z1 [R, T, H/group] fp16 bits)."""
+    _dev_tensor(x, "x")
+    R, T, H = x.shape
+    dev = x.device
+    if codes1 is None:
+        codes1 = torch.empty((R, T, H * bits // 8), dtype=torch.uint8, device=dev)
+    if s1 is None:
+        s1 = torch.empty((R, T, max(H // group, 0)), dtype=torch.uint16, device=dev)
+    if z1 is None:
+        z1 = torch.empty_like(s1)
+    _check(lib().fc_quantize_groups(_ptr(x), _DTYPES[x.dtype], R, T, H, bits, group, _ptr(codes1),
+                                    _ptr(s1), _ptr(z1), _stream(stream, dev)), "fc_quantize_groups")
+    return codes1, s1, z1
+
+
+def fc_dequant_sum_requant(codes1, s1, z1, R: int, T: int, H: int, bits: int, group: int,
+                           codes2=None, s2=None, z2=None, stream=None):
+    """Stage-1 payload -> (codes2 [T, H*bits/8], s2, z2 [T, H/g2])."""
+    for n, t in (("codes1", codes1), ("s1", s1), ("z1", z1)):
+        _dev_tensor(t, n)
+    dev = codes1.device
+    g2 = fc_stage2_group(R, H, group)
+    if codes2 is None:
+        codes2 = torch.empty((T, H * bits // 8), dtype=torch.uint8, device=dev)
+    if s2 is None:
+        s2 = torch.empty((T, H // g2 if g2 else 0), dtype=torch.uint16, device=dev)
+    if z2 is None:
+        z2 = torch.empty_like(s2)
+    _check(lib().fc_dequant_sum_requant(_ptr(codes1), _ptr(s1), _ptr(z1), R, T, H, bits, group,
+                                        _ptr(codes2), _ptr(s2), _ptr(z2), _stream(stream, dev)),
+           "fc_dequant_sum_requant")
+    return codes2, s2, z2
+
+
+def fc_dequantize(codes2, s2, z2, T: int, H: int, bits: int, group2: int, dtype: torch.dtype,
+                  out=None, stream=None):
+    """Stage-2 payload -> out [T, H] of `dtype`."""
+    for n, t in (("codes2", codes2), ("s2", s2), ("z2", z2)):
+        _dev_tensor(t, n)
+    dev = codes2.device
+    if out is None:
+        out = torch.empty((T, H), dtype=dtype, device=dev)
+    _check(lib().fc_dequantize(_ptr(codes2), _ptr(s2), _ptr(z2), T, H, bits, group2,
+                               _DTYPES[out.dtype], _ptr(out), _stream(stream, dev)), "fc_dequantize")
+    return out
+
+
+def fc_allreduce_emulated(x: torch.Tensor, bits: int, group: int, out=None, workspace=None,
+                          stream=None):
+    """x [R, T, H] -> out [T, H]: the whole emulated all-reduce (three kernels)."""
+    _dev_tensor(x, "x")
+    R, T, H = x.shape
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(fc_workspace_bytes(R, T, H, bits, group), 1), dtype=torch.uint8,
+                                device=dev)
+    _check(lib().fc_allreduce_emulated(_ptr(x), _DTYPES[x.dtype], R, T, H, bits, group, _ptr(out),
+                                       _ptr(workspace), workspace.numel(), _stream(stream, dev)),
+           "fc_allreduce_emulated")
+    return out, workspace
+
+
+def workspace_views(workspace: torch.Tensor, R: int, T: int, H: int, bits: int, group: int) -> dict:
+    """Views of the payloads inside an fc_allreduce_emulated workspace."""
+    lay = fc_workspace_layout(R, T, H, bits, group)
+    g2 = fc_stage2_group(R, H, group)
+    names = ("codes1", "s1", "z1", "codes2", "s2", "z2")
+    shapes = ((R, T, H * bits // 8), (R, T, H // group), (R, T, H // group),
+              (T, H * bits // 8), (T, H // g2), (T, H // g2))
+    out = {}
+    for name, (off, size), shape in zip(names, lay, shapes):
+        raw = workspace[off:off + size]
+        out[name] = raw.view(torch.uint16).view(shape) if name[0] in "sz" else raw.view(shape)
+    return out

@@ -1,0 +1,77 @@
+// Final dequantization after the All-Gather of "Flash Communication:
+// Reducing Tensor Parallelization Bottleneck for Fast Large Language Model
+// Inference" (Figure 5, right): every rank holds all R requantized chunks and
+// expands them to 16-bit activations, out = round_half_even(fp32(q*s + z)).
+//
+// HBM-bound: per element it reads bits/8 code bytes (plus 4 bytes per group)
+// and writes 2 bytes.
+#include "fc_device.h"
+#include "fc_launch.h"
+
+namespace fc {
+namespace {
+
+constexpr int kSlots = 4;
+
+template <int DT, int BITS>
+__global__ __launch_bounds__(kBlockThreads) void dequant_kernel(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ s,
+    const uint16_t *__restrict__ z, uint64_t n, int g_shift, uint16_t *__restrict__ out) {
+    constexpr int W = BITS == 4 ? 1 : 2;
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t wave = (uint64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+    const uint64_t tile = wave * (uint64_t)(kSlots * kSlotElems);
+    if (tile >= n) return;
+
+    uint32_t w[kSlots][W];
+    uint16_t sb[kSlots], zb[kSlots];
+    bool ok[kSlots];
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+        const uint64_t e = tile + (uint64_t)(u * kSlotElems + lane * kLaneElems);
+        ok[u] = e < n;
+        if (ok[u]) {
+            load_codes<BITS>(codes, e, w[u]);
+            sb[u] = s[e >> g_shift];
+            zb[u] = z[e >> g_shift];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+        if (!ok[u]) continue;
+        const uint64_t e = tile + (uint64_t)(u * kSlotElems + lane * kLaneElems);
+        float q[kLaneElems], o[kLaneElems];
+        decode8<BITS>(w[u], q);
+        const float sv = half_bits_to_float(sb[u]);
+        const float zv = half_bits_to_float(zb[u]);
+#pragma unroll
+        for (int k = 0; k < kLaneElems; ++k) o[k] = __builtin_fmaf(q[k], sv, zv);   // exact product
+        *reinterpret_cast<uint4 *>(out + e) = narrow8<DT>(o);
+    }
+}
+
+template <int DT, int BITS>
+hipError_t launch_one(const uint8_t *codes, const uint16_t *s, const uint16_t *z, uint64_t n,
+                      int g_shift, uint16_t *out, hipStream_t stream) {
+    constexpr uint64_t per_block = (uint64_t)kWavesPerBlock * kSlots * kSlotElems;
+    const uint64_t blocks = (n + per_block - 1) / per_block;
+    if (blocks > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((dequant_kernel<DT, BITS>), dim3((unsigned)blocks), dim3(kBlockThreads), 0,
+                       stream, codes, s, z, n, g_shift, out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dequantize(const uint8_t *codes2, const uint16_t *s2, const uint16_t *z2,
+                             uint64_t n, int bits, int group2, int dtype, uint16_t *out,
+                             hipStream_t stream) {
+    const int sh = ilog2(group2);
+    if (dtype == 0)
+        return bits == 4 ? launch_one<0, 4>(codes2, s2, z2, n, sh, out, stream)
+                         : launch_one<0, 8>(codes2, s2, z2, n, sh, out, stream);
+    return bits == 4 ? launch_one<1, 4>(codes2, s2, z2, n, sh, out, stream)
+                     : launch_one<1, 8>(codes2, s2, z2, n, sh, out, stream);
+}
+
+}  // namespace fc

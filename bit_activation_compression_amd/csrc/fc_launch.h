@@ -1,0 +1,27 @@
+// Internal launchers of the codec kernels (one per kernel family). Arguments
+// are validated by the C ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fc {
+
+// Stage-1 quantizer over n consecutive 16-bit values in groups of `group`
+// (n % group == 0): codes [n*bits/8], s, z [n/group].
+hipError_t launch_quantize(const uint16_t *x, int dtype, uint64_t n, int bits, int group,
+                           uint8_t *codes, uint16_t *s, uint16_t *z, hipStream_t stream);
+
+// Reduce-scatter reduction + requantization over n = T*H positions of R
+// operands laid out [R][n]: stage-1 groups of `group1`, stage-2 groups of `group2`.
+hipError_t launch_dequant_sum_requant(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1,
+                                      int R, uint64_t n, int bits, int group1, int group2,
+                                      uint8_t *codes2, uint16_t *s2, uint16_t *z2,
+                                      hipStream_t stream);
+
+// Final dequantization of n codes in groups of `group2` into 16-bit outputs.
+hipError_t launch_dequantize(const uint8_t *codes2, const uint16_t *s2, const uint16_t *z2,
+                             uint64_t n, int bits, int group2, int dtype, uint16_t *out,
+                             hipStream_t stream);
+
+}  // namespace fc

@@ -1,0 +1,134 @@
+/*
+ * fc.h -- C ABI of a low-bit all-reduce codec for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one of "Flash Communication: Reducing Tensor
+ * Parallelization Bottleneck for Fast Large Language Model Inference":
+ *   - TL;DR and Abstract: the activations exchanged by a tensor-parallel
+ *     all-reduce travel as low-bit codes, and the all-reduce runs in two
+ *     steps instead of a ring;
+ *   - Figure 5 (right): the two steps are a Reduce-Scatter (RS) and an
+ *     All-Gather (AG), and the activations are quantized before each;
+ *   - Figure 4: quantization is block-wise along the hidden dimension, with
+ *     block sizes from the full hidden length down to 128.
+ * The page gives no formula; this library implements the asymmetric min/max
+ * reading (integer codes with an fp16 scale and an fp16 zero point per group,
+ * rounded half to even), identical bit for bit to the project's CPU oracle:
+ *
+ *   per group:  mn, mx = min, max (a zero result taken as +0)
+ *               s = fp16(fp32(fp32(mx - mn) / Q)),  z = fp16(mn),  Q = 2^bits - 1
+ *               inv = fp32(1 / s), or 0 when s == 0
+ *               q = clamp(round_half_even(fp32(fp32(v - z) * inv)), 0, Q)
+ *   dequantize: v' = fp32(q * s + z)            (q * s is exact)
+ *
+ * All R operands live on one GPU: operand r is the partial sum that rank r of
+ * a TP group of size R would hold. Hidden chunk j (columns [j*C, (j+1)*C),
+ * C = H/R) is the part that rank j reduces in the RS step.
+ *
+ * Conventions for every entry point:
+ *   - Buffer pointers are DEVICE pointers, owned by the caller; the library
+ *     never keeps, frees or allocates them, and allocates nothing itself.
+ *   - `stream` is a hipStream_t (NULL means the default stream). Calls are
+ *     asynchronous: they return once the kernels are enqueued. On any
+ *     validation error nothing is enqueued and no buffer is written.
+ *   - All device pointers must be 16-byte aligned (FC_ERR_ALIGN otherwise).
+ *   - Layouts are dense row-major. 8-bit codes take one byte each; 4-bit
+ *     codes take two per byte, the even element in the low nibble.
+ *     Scales and zeros are raw IEEE binary16 bit patterns, separate arrays.
+ *   - T == 0 is valid and enqueues nothing (pointers may then be NULL).
+ *   - Non-finite inputs, or inputs whose scale or zero overflow fp16
+ *     (|min| > 65504 or (max - min)/Q > 65504), are outside the contract:
+ *     the results are unspecified but every access stays in bounds.
+ *   - No global state: concurrent calls on different streams are safe.
+ *
+ * Supported shapes (FC_ERR_SHAPE otherwise): R >= 1, T >= 0, H >= 1,
+ * bits in {4, 8} (FC_ERR_BITS), group a power of two in [8, 8192] dividing H,
+ * H % R == 0, and the stage-2 group g2 = min(group, H/R) a power of two in
+ * [8, 8192] dividing H/R.
+ */
+#ifndef FC_H_
+#define FC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FC_OK = 0,
+    FC_ERR_NULL = 1,       /* a required pointer is NULL */
+    FC_ERR_SHAPE = 2,      /* R, T, H, group or chunking outside the supported set */
+    FC_ERR_BITS = 3,       /* bits is not 4 or 8 */
+    FC_ERR_ALIGN = 4,      /* a device pointer is not 16-byte aligned */
+    FC_ERR_WORKSPACE = 5,  /* workspace smaller than fc_workspace_bytes() */
+    FC_ERR_LAUNCH = 6,     /* the HIP runtime reported an error at launch */
+    FC_ERR_DTYPE = 7       /* dtype is not FC_F16 or FC_BF16 */
+} fc_status;
+
+typedef enum { FC_F16 = 0, FC_BF16 = 1 } fc_dtype;
+
+/*
+ * Quantize before the Reduce-Scatter (Figure 5, right; groups as in Figure 4).
+ *   x      [R][T][H]            fp16 or bf16 (dt)
+ *   codes1 [R][T][H*bits/8]     uint8
+ *   s1, z1 [R][T][H/group]      fp16 bit patterns
+ * Every (r, t, k) group of `group` consecutive hidden columns is quantized on
+ * its own.
+ */
+fc_status fc_quantize_groups(const void *x, fc_dtype dt, int R, int T, int H, int bits, int group,
+                             uint8_t *codes1, uint16_t *s1, uint16_t *z1, void *stream);
+
+/*
+ * The Reduce-Scatter reduction and the quantization before the All-Gather
+ * (Figure 5, right; TL;DR "two-step All-Reduce").
+ *   codes1, s1, z1  as produced by fc_quantize_groups
+ *   codes2 [T][H*bits/8], s2, z2 [T][H/g2] with g2 = fc_stage2_group(R, H, group)
+ * For each chunk j, token t and column h of the chunk, the R operands are
+ * dequantized with their own stage-1 scale and zero and summed in binary32 in
+ * ascending r starting from operand 0; the sums are requantized in groups of
+ * g2 consecutive columns (never crossing a chunk).
+ */
+fc_status fc_dequant_sum_requant(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1,
+                                 int R, int T, int H, int bits, int group,
+                                 uint8_t *codes2, uint16_t *s2, uint16_t *z2, void *stream);
+
+/*
+ * Dequantize after the All-Gather (Figure 5, right).
+ *   codes2 [T][H*bits/8], s2, z2 [T][H/group2]  ->  out [T][H] in dt
+ * out = round_half_even_to_dt(fp32(q * s + z)).
+ * group2 must be a power of two in [8, 8192] dividing H.
+ */
+fc_status fc_dequantize(const uint8_t *codes2, const uint16_t *s2, const uint16_t *z2,
+                        int T, int H, int bits, int group2, fc_dtype dt, void *out, void *stream);
+
+/*
+ * The whole emulated all-reduce on one GPU: fc_quantize_groups, then
+ * fc_dequant_sum_requant, then fc_dequantize, with both payloads placed in the
+ * caller's workspace (layout: fc_workspace_layout). out [T][H] in dt.
+ */
+fc_status fc_allreduce_emulated(const void *x, fc_dtype dt, int R, int T, int H, int bits, int group,
+                                void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace fc_allreduce_emulated needs; 0 if the arguments are unsupported. */
+size_t fc_workspace_bytes(int R, int T, int H, int bits, int group);
+
+/*
+ * Byte offsets and sizes of the six workspace slices, in this order:
+ * codes1, s1, z1, codes2, s2, z2. Each offset is a multiple of 256.
+ * Host-only; touches no device memory.
+ */
+fc_status fc_workspace_layout(int R, int T, int H, int bits, int group,
+                              size_t offsets[6], size_t sizes[6]);
+
+/* Stage-2 group length min(group, H/R); 0 if the arguments are unsupported. */
+int fc_stage2_group(int R, int H, int group);
+
+/* A static string naming the status. */
+const char *fc_status_string(fc_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FC_H_ */

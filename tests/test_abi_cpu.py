@@ -1,0 +1,106 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/fc.h declares, lays out the workspace as documented, and rejects
+unsupported arguments before touching any device pointer (the pointers
+passed here are fake, 16-byte aligned host integers; a validation bug would
+surface as a HIP error, not as a write)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_activation_compression_amd as fc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fc.h")
+
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced on the error paths
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fc_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = fc.lib()
+    names = _declared_functions()
+    assert len(names) == 8
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(names) == sorted(fc.EXPORTED_SYMBOLS)
+
+
+def test_status_strings():
+    for s in range(8):
+        assert fc.fc_status_string(s).startswith("FC_")
+    assert "unknown" in fc.fc_status_string(99)
+
+
+def test_stage2_group():
+    assert fc.fc_stage2_group(4, 8192, 128) == 128
+    assert fc.fc_stage2_group(4, 4096, 4096) == 1024
+    assert fc.fc_stage2_group(2, 256, 128) == 128
+    assert fc.fc_stage2_group(3, 4096, 128) == 0         # H % R != 0
+    assert fc.fc_stage2_group(4, 4096, 96) == 0          # not a power of two
+    assert fc.fc_stage2_group(4, 64, 64) == 16
+    assert fc.fc_stage2_group(64, 512, 8) == 8
+    assert fc.fc_stage2_group(128, 512, 8) == 0
+
+
+def test_workspace_layout_matches_payload_sizes():
+    R, T, H, bits, g = 4, 8192, 8192, 4, 128
+    lay = fc.fc_workspace_layout(R, T, H, bits, g)
+    sizes = [s for _, s in lay]
+    assert sizes == [R * T * H // 2, R * T * H // g * 2, R * T * H // g * 2,
+                     T * H // 2, T * H // g * 2, T * H // g * 2]
+    offs = [o for o, _ in lay]
+    assert all(o % 256 == 0 for o in offs)
+    assert all(offs[i] + sizes[i] <= offs[i + 1] for i in range(5))
+    total = fc.fc_workspace_bytes(R, T, H, bits, g)
+    assert total >= offs[5] + sizes[5] and total - (offs[5] + sizes[5]) < 256
+    assert fc.fc_workspace_bytes(4, 8192, 8192, 5, 128) == 0
+
+
+def _q(*args):
+    return fc.lib().fc_quantize_groups(*args)
+
+
+@pytest.mark.parametrize("R,T,H,bits,g,status", [
+    (4, 8, 512, 5, 128, 3),       # bits
+    (4, 8, 512, 4, 96, 2),        # group not a power of two
+    (4, 8, 512, 4, 4, 2),         # group below 8
+    (4, 8, 512, 4, 16384, 2),     # group above 8192
+    (4, 8, 512, 4, 1024, 2),      # group does not divide H
+    (3, 8, 512, 4, 128, 2),       # H % R
+    (0, 8, 512, 4, 128, 2),       # R
+    (4, -1, 512, 4, 128, 2),      # T
+    (128, 8, 512, 4, 8, 2),       # C = 4 gives g2 = 4 < 8
+])
+def test_quantize_rejects_bad_shapes(R, T, H, bits, g, status):
+    assert _q(FAKE, 0, R, T, H, bits, g, FAKE, FAKE, FAKE, None) == status
+
+
+def test_pointer_checks_before_launch():
+    assert _q(None, 0, 2, 8, 256, 8, 128, FAKE, FAKE, FAKE, None) == 1
+    assert _q(FAKE, 0, 2, 8, 256, 8, 128, FAKE, None, FAKE, None) == 1
+    assert _q(MISALIGNED, 0, 2, 8, 256, 8, 128, FAKE, FAKE, FAKE, None) == 4
+    assert _q(FAKE, 0, 2, 8, 256, 8, 128, FAKE, FAKE, MISALIGNED, None) == 4
+    assert _q(FAKE, 2, 2, 8, 256, 8, 128, FAKE, FAKE, FAKE, None) == 7   # dtype
+    # T == 0: nothing to do, NULL pointers allowed
+    assert _q(None, 0, 2, 0, 256, 8, 128, None, None, None, None) == 0
+
+
+def test_other_entry_points_validate():
+    L = fc.lib()
+    assert L.fc_dequant_sum_requant(FAKE, FAKE, FAKE, 3, 8, 256, 4, 128, FAKE, FAKE, FAKE, None) == 2
+    assert L.fc_dequant_sum_requant(FAKE, FAKE, None, 2, 8, 256, 4, 128, FAKE, FAKE, FAKE, None) == 1
+    assert L.fc_dequantize(FAKE, FAKE, FAKE, 8, 256, 4, 96, 0, FAKE, None) == 2
+    assert L.fc_dequantize(FAKE, FAKE, FAKE, 8, 256, 6, 128, 0, FAKE, None) == 3
+    assert L.fc_dequantize(FAKE, FAKE, FAKE, 8, 256, 4, 128, 0, MISALIGNED, None) == 4
+    need = fc.fc_workspace_bytes(2, 8, 256, 8, 128)
+    assert L.fc_allreduce_emulated(FAKE, 0, 2, 8, 256, 8, 128, FAKE, FAKE, need - 1, None) == 5
+    assert L.fc_allreduce_emulated(FAKE, 0, 2, 8, 256, 8, 128, None, FAKE, need, None) == 1
+    assert L.fc_allreduce_emulated(None, 0, 2, 0, 256, 8, 128, None, None, 0, None) == 0
