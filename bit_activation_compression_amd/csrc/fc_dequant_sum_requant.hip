@@ -13,81 +13,111 @@
 //
 // Per output element it reads R*bits/8 code bytes (plus 4 bytes per stage-1
 // group and operand) and writes bits/8 code bytes (plus 4 per stage-2 group).
-// The fp32 work per element grows with R (decode, fma, add per operand).
+// The fp32 work per element grows with R (decode, fma, add per operand), so
+// for R = 4 the kernel is bound by vector ALU issue rather than by HBM.
 #include "fc_device.h"
 #include "fc_launch.h"
 
 namespace fc {
 namespace {
 
-constexpr int kOperandBatch = 4;   // operands whose loads are in flight together
+// RT > 0: the operand count is a compile-time constant (all loads of a tile
+// are issued before the first use); RT == 0: any R, one operand at a time.
+constexpr int base_slots(int RT) { return RT >= 8 ? 2 : 4; }
 
-template <int BITS, int G2>
+template <int BITS, int G2, int RT>
 __global__ __launch_bounds__(kBlockThreads) void dsr_kernel(
     const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ s1,
-    const uint16_t *__restrict__ z1, int R, uint64_t n, int g1_shift,
+    const uint16_t *__restrict__ z1, int R_arg, uint64_t n, int g1_shift,
     uint8_t *__restrict__ codes2, uint16_t *__restrict__ s2, uint16_t *__restrict__ z2) {
-    constexpr int U = tile_slots(G2);
+    constexpr int U = tile_slots(G2, base_slots(RT));
     constexpr int S = G2 > kSlotElems ? G2 / kSlotElems : 1;
     constexpr int L = G2 >= kSlotElems ? kWave : G2 / kLaneElems;
     constexpr int W = BITS == 4 ? 1 : 2;
-    static_assert(U % S == 0, "a tile holds whole groups");
+    static_assert(U % S == 0 && (U * kSlotElems) % G2 == 0, "a tile holds whole groups");
+    const int R = RT > 0 ? RT : R_arg;
 
     const int lane = threadIdx.x & (kWave - 1);
     const uint64_t wave = (uint64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
     const uint64_t tile = wave * (uint64_t)(U * kSlotElems);
     if (tile >= n) return;
+    const uint64_t left = n - tile;
+    const uint32_t avail = left < (uint64_t)(U * kSlotElems) ? (uint32_t)left : U * kSlotElems;
 
+    // Stage-1 metadata index of element (r, tile + rel):
+    //   ((r*n + tile) >> s) + (((tile mod 2^s) + rel) >> s),
+    // since r*n is a multiple of the stage-1 group; the second term is the
+    // same for every operand.
+    // Lanes past the end of the data (last tile only) load the tile's first
+    // element instead, so every load is unconditional and all of a tile's
+    // loads are in flight together; only their stores are skipped.
+    const uint32_t mis = (uint32_t)tile & ((1u << g1_shift) - 1u);
+    uint32_t rel[U], lrel[U], mrel[U];
     bool ok[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-        ok[u] = tile + (uint64_t)(u * kSlotElems + lane * kLaneElems) < n;
+    for (int u = 0; u < U; ++u) {
+        rel[u] = u * kSlotElems + lane * kLaneElems;
+        ok[u] = rel[u] < avail;
+        lrel[u] = ok[u] ? rel[u] : 0u;
+        mrel[u] = (mis + lrel[u]) >> g1_shift;
+    }
 
-    float y[U][kLaneElems] = {};
-    for (int r0 = 0; r0 < R; r0 += kOperandBatch) {
-        uint32_t w[kOperandBatch][U][W];
-        uint16_t sb[kOperandBatch][U], zb[kOperandBatch][U];
+    float y[U][kLaneElems];
+    auto load_operand = [&](int r, uint32_t (&w)[U][W], uint16_t (&sv)[U], uint16_t (&zv)[U]) {
+        const uint64_t e0 = (uint64_t)r * n + tile;
+        const uint8_t *cb = codes1 + e0 * BITS / 8;
+        const uint16_t *sb = s1 + (e0 >> g1_shift);
+        const uint16_t *zb = z1 + (e0 >> g1_shift);
 #pragma unroll
-        for (int i = 0; i < kOperandBatch; ++i) {
-            if (r0 + i >= R) break;
-            const uint64_t base = (uint64_t)(r0 + i) * n;
+        for (int u = 0; u < U; ++u) {
+            load_codes<BITS, false>(cb, lrel[u], w[u]);
+            sv[u] = sb[mrel[u]];
+            zv[u] = zb[mrel[u]];
+        }
+    };
+    // x_hat = fp32(q*s + z): q*s is exact (<= 8 x 11 significant bits), so
+    // the fused multiply-add rounds exactly once, as the method does.
+    auto add_operand = [&](bool first, const uint32_t (&w)[U][W], const uint16_t (&sv)[U],
+                           const uint16_t (&zv)[U]) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint64_t e = base + tile + (uint64_t)(u * kSlotElems + lane * kLaneElems);
-                if (ok[u]) {
-                    load_codes<BITS>(codes1, e, w[i][u]);
-                    sb[i][u] = s1[e >> g1_shift];
-                    zb[i][u] = z1[e >> g1_shift];
-                } else {
+        for (int u = 0; u < U; ++u) {
+            float q[kLaneElems];
+            decode8<BITS>(w[u], q);
+            const float s = half_bits_to_float(sv[u]);
+            const float z = half_bits_to_float(zv[u]);
 #pragma unroll
-                    for (int k = 0; k < W; ++k) w[i][u][k] = 0;
-                    sb[i][u] = 0;
-                    zb[i][u] = 0;
-                }
+            for (int k = 0; k < kLaneElems; ++k) {
+                const float xh = __builtin_fmaf(q[k], s, z);
+                y[u][k] = first ? xh : y[u][k] + xh;
             }
         }
+    };
+
+    if constexpr (RT > 0) {
+        uint32_t w[RT][U][W];
+        uint16_t sv[RT][U], zv[RT][U];
 #pragma unroll
-        for (int i = 0; i < kOperandBatch; ++i) {
-            if (r0 + i >= R) break;
+        for (int r = 0; r < RT; ++r) load_operand(r, w[r], sv[r], zv[r]);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float q[kLaneElems];
-                decode8<BITS>(w[i][u], q);
-                const float s = half_bits_to_float(sb[i][u]);
-                const float z = half_bits_to_float(zb[i][u]);
-#pragma unroll
-                for (int k = 0; k < kLaneElems; ++k) {
-                    const float xh = __builtin_fmaf(q[k], s, z);   // q*s exact: equals fp32(q*s + z)
-                    y[u][k] = (r0 + i == 0) ? xh : y[u][k] + xh;
-                }
-            }
+        for (int r = 0; r < RT; ++r) add_operand(r == 0, w[r], sv[r], zv[r]);
+    } else {
+        uint32_t w[U][W];
+        uint16_t sv[U], zv[U];
+        load_operand(0, w, sv, zv);
+        add_operand(true, w, sv, zv);
+        for (int r = 1; r < R; ++r) {
+            load_operand(r, w, sv, zv);
+            add_operand(false, w, sv, zv);
         }
     }
 
+    // requantize the sums in groups of G2 (tiles start on a group boundary)
+    uint8_t *cb = codes2 + tile * BITS / 8;
+    uint16_t *sb = s2 + tile / G2;
+    uint16_t *zb = z2 + tile / G2;
     float mn[U], mx[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) minmax8(y[u], mn[u], mx[u]);
-
 #pragma unroll
     for (int g = 0; g < U / S; ++g) {
         float a = mn[g * S], b = mx[g * S];
@@ -101,39 +131,54 @@ __global__ __launch_bounds__(kBlockThreads) void dsr_kernel(
 #pragma unroll
         for (int k = 0; k < S; ++k) {
             const int u = g * S + k;
-            const uint64_t e = tile + (uint64_t)(u * kSlotElems + lane * kLaneElems);
             if (!ok[u]) continue;
             uint32_t w[W];
             encode8<BITS>(y[u], p, w);
-            store_codes<BITS>(codes2, e, w);
+            store_codes<BITS, false>(cb, rel[u], w);
             const bool leader = (S > 1) ? (k == 0 && lane == 0) : (lane % L == 0);
             if (leader) {
-                const uint64_t m = e / G2;
-                s2[m] = p.s16;
-                z2[m] = p.z16;
+                sb[rel[u] / G2] = p.s16;
+                zb[rel[u] / G2] = p.z16;
             }
         }
     }
 }
 
-template <int BITS, int G2>
+template <int BITS, int G2, int RT>
 hipError_t launch_one(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1, int R,
                       uint64_t n, int g1_shift, uint8_t *codes2, uint16_t *s2, uint16_t *z2,
                       hipStream_t stream) {
-    constexpr uint64_t per_block = (uint64_t)kWavesPerBlock * tile_slots(G2) * kSlotElems;
+    constexpr uint64_t per_block =
+        (uint64_t)kWavesPerBlock * tile_slots(G2, base_slots(RT)) * kSlotElems;
     const uint64_t blocks = (n + per_block - 1) / per_block;
     if (blocks > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((dsr_kernel<BITS, G2>), dim3((unsigned)blocks), dim3(kBlockThreads), 0, stream,
-                       codes1, s1, z1, R, n, g1_shift, codes2, s2, z2);
+    hipLaunchKernelGGL((dsr_kernel<BITS, G2, RT>), dim3((unsigned)blocks), dim3(kBlockThreads), 0,
+                       stream, codes1, s1, z1, R, n, g1_shift, codes2, s2, z2);
     return hipGetLastError();
+}
+
+template <int BITS, int G2>
+hipError_t dispatch_r(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1, int R,
+                      uint64_t n, int g1_shift, uint8_t *codes2, uint16_t *s2, uint16_t *z2,
+                      hipStream_t stream) {
+    // The compile-time operand count keeps R x U code words in flight; it is
+    // used only where a tile is the base size, so registers stay bounded.
+    if constexpr (G2 <= kSlotElems * base_slots(8)) {
+        if (R == 8) return launch_one<BITS, G2, 8>(codes1, s1, z1, R, n, g1_shift, codes2, s2, z2, stream);
+    }
+    if constexpr (G2 <= kSlotElems * base_slots(4)) {
+        if (R == 4) return launch_one<BITS, G2, 4>(codes1, s1, z1, R, n, g1_shift, codes2, s2, z2, stream);
+        if (R == 2) return launch_one<BITS, G2, 2>(codes1, s1, z1, R, n, g1_shift, codes2, s2, z2, stream);
+    }
+    return launch_one<BITS, G2, 0>(codes1, s1, z1, R, n, g1_shift, codes2, s2, z2, stream);
 }
 
 template <int BITS>
 hipError_t dispatch_group(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1, int R,
                           uint64_t n, int g1_shift, int group2, uint8_t *codes2, uint16_t *s2,
                           uint16_t *z2, hipStream_t stream) {
-#define FC_CASE(G)                                                                               \
-    case G: return launch_one<BITS, G>(codes1, s1, z1, R, n, g1_shift, codes2, s2, z2, stream);
+#define FC_CASE(G) \
+    case G: return dispatch_r<BITS, G>(codes1, s1, z1, R, n, g1_shift, codes2, s2, z2, stream);
     switch (group2) {
         FC_CASE(8) FC_CASE(16) FC_CASE(32) FC_CASE(64) FC_CASE(128) FC_CASE(256) FC_CASE(512)
         FC_CASE(1024) FC_CASE(2048) FC_CASE(4096) FC_CASE(8192)

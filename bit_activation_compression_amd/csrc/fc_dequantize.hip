@@ -22,31 +22,39 @@ __global__ __launch_bounds__(kBlockThreads) void dequant_kernel(
     const uint64_t wave = (uint64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
     const uint64_t tile = wave * (uint64_t)(kSlots * kSlotElems);
     if (tile >= n) return;
+    const uint64_t left = n - tile;
+    const uint32_t avail = left < (uint64_t)(kSlots * kSlotElems) ? (uint32_t)left : kSlots * kSlotElems;
+    // group index of element tile + rel: (tile >> s) + (((tile mod 2^s) + rel) >> s)
+    const uint32_t mis = (uint32_t)tile & ((1u << g_shift) - 1u);
+    const uint8_t *cb = codes + tile * BITS / 8;
+    const uint16_t *sb = s + (tile >> g_shift);
+    const uint16_t *zb = z + (tile >> g_shift);
+    uint16_t *ob = out + tile;
 
     uint32_t w[kSlots][W];
-    uint16_t sb[kSlots], zb[kSlots];
-    bool ok[kSlots];
+    uint16_t sv[kSlots], zv[kSlots];
+    // lanes past the end of the data load the tile's first element instead
+    // (unconditional loads, all in flight together); their stores are skipped
 #pragma unroll
     for (int u = 0; u < kSlots; ++u) {
-        const uint64_t e = tile + (uint64_t)(u * kSlotElems + lane * kLaneElems);
-        ok[u] = e < n;
-        if (ok[u]) {
-            load_codes<BITS>(codes, e, w[u]);
-            sb[u] = s[e >> g_shift];
-            zb[u] = z[e >> g_shift];
-        }
+        const uint32_t rel = u * kSlotElems + lane * kLaneElems;
+        const uint32_t lrel = rel < avail ? rel : 0u;
+        load_codes<BITS, false>(cb, lrel, w[u]);
+        const uint32_t m = (mis + lrel) >> g_shift;
+        sv[u] = sb[m];
+        zv[u] = zb[m];
     }
 #pragma unroll
     for (int u = 0; u < kSlots; ++u) {
-        if (!ok[u]) continue;
-        const uint64_t e = tile + (uint64_t)(u * kSlotElems + lane * kLaneElems);
+        const uint32_t rel = u * kSlotElems + lane * kLaneElems;
+        if (rel >= avail) continue;
         float q[kLaneElems], o[kLaneElems];
         decode8<BITS>(w[u], q);
-        const float sv = half_bits_to_float(sb[u]);
-        const float zv = half_bits_to_float(zb[u]);
+        const float sf = half_bits_to_float(sv[u]);
+        const float zf = half_bits_to_float(zv[u]);
 #pragma unroll
-        for (int k = 0; k < kLaneElems; ++k) o[k] = __builtin_fmaf(q[k], sv, zv);   // exact product
-        *reinterpret_cast<uint4 *>(out + e) = narrow8<DT>(o);
+        for (int k = 0; k < kLaneElems; ++k) o[k] = __builtin_fmaf(q[k], sf, zf);   // exact product
+        stv<u32x4, false>(ob, rel * 2, narrow8<DT>(o));
     }
 }
 

@@ -10,6 +10,9 @@
 // are reduced first inside the lane, then across lanes with DPP row
 // operations (<= 16 lanes), ds_swizzle (32 lanes) and readlane (64 lanes).
 //
+// Addresses are a wave-uniform base (SGPRs) plus a 32-bit per-lane offset,
+// so no lane does 64-bit address arithmetic.
+//
 // Arithmetic follows the quantizer of "Flash Communication: Reducing Tensor
 // Parallelization Bottleneck for Fast Large Language Model Inference"
 // (Figures 4 and 5) in the asymmetric min/max reading: every binary32
@@ -31,12 +34,72 @@ constexpr int kWavesPerBlock = kBlockThreads / kWave;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v >> 1); }
 
-// Slots a wave processes per tile for group length G: at least 4 (16 KiB of
-// bf16 in flight per wave) and a whole number of groups.
-constexpr int tile_slots(int G) { return G > 4 * kSlotElems ? G / kSlotElems : 4; }
+// Slots a wave processes per tile for group length G: at least `base` and a
+// whole number of groups.
+constexpr int tile_slots(int G, int base) { return G > base * kSlotElems ? G / kSlotElems : base; }
+
+// Hides a value from the optimizer (no instruction is emitted).
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm("" : "+v"(v));
+    return v;
+}
+
+// Pins v as a rounded binary32 register value. Without it the compiler may
+// fuse the fma that produced v with a following fp32 -> fp16 conversion into
+// one mixed-precision instruction (v_fma_mixlo_f16) that rounds once, straight
+// to fp16, where the method rounds to binary32 first and then to fp16.
+__device__ __forceinline__ float as_f32(float v) {
+    asm("" : "+v"(v));
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// memory access at a wave-uniform base plus a 32-bit per-lane byte offset;
+// NT marks streamed data non-temporal
+// ---------------------------------------------------------------------------
+
+template <typename V, bool NT>
+__device__ __forceinline__ V ldv(const void *base, uint32_t byte_off) {
+    const V *p = reinterpret_cast<const V *>(static_cast<const uint8_t *>(base) + byte_off);
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <typename V, bool NT>
+__device__ __forceinline__ void stv(void *base, uint32_t byte_off, V v) {
+    V *p = reinterpret_cast<V *>(static_cast<uint8_t *>(base) + byte_off);
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+// The lane's 8 codes at element offset `rel` from a wave-uniform base.
+template <int BITS, bool NT>
+__device__ __forceinline__ void load_codes(const uint8_t *base, uint32_t rel,
+                                           uint32_t (&w)[BITS == 4 ? 1 : 2]) {
+    if constexpr (BITS == 8) {
+        const u32x2 v = ldv<u32x2, NT>(base, rel);
+        w[0] = v.x;
+        w[1] = v.y;
+    } else {
+        w[0] = ldv<uint32_t, NT>(base, rel / 2);
+    }
+}
+
+template <int BITS, bool NT>
+__device__ __forceinline__ void store_codes(uint8_t *base, uint32_t rel,
+                                            const uint32_t (&w)[BITS == 4 ? 1 : 2]) {
+    if constexpr (BITS == 8) {
+        const u32x2 v = {w[0], w[1]};
+        stv<u32x2, NT>(base, rel, v);
+    } else {
+        stv<uint32_t, NT>(base, rel / 2, w[0]);
+    }
+}
 
 // ---------------------------------------------------------------------------
 // cross-lane min/max
@@ -85,11 +148,14 @@ __device__ __forceinline__ void lanes_minmax(float &mn, float &mx) {
     }
 }
 
+// In-lane min and max of 8 values (chains of three-input v_min3/v_max3).
 __device__ __forceinline__ void minmax8(const float (&v)[kLaneElems], float &mn, float &mx) {
-    mn = __builtin_fminf(__builtin_fminf(__builtin_fminf(v[0], v[1]), __builtin_fminf(v[2], v[3])),
-                         __builtin_fminf(__builtin_fminf(v[4], v[5]), __builtin_fminf(v[6], v[7])));
-    mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), __builtin_fmaxf(v[2], v[3])),
-                         __builtin_fmaxf(__builtin_fmaxf(v[4], v[5]), __builtin_fmaxf(v[6], v[7])));
+    mn = __builtin_fminf(__builtin_fminf(__builtin_fminf(__builtin_fminf(v[0], v[1]), v[2]),
+                                         __builtin_fminf(v[3], v[4])),
+                         __builtin_fminf(__builtin_fminf(v[5], v[6]), v[7]));
+    mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]),
+                                         __builtin_fmaxf(v[3], v[4])),
+                         __builtin_fmaxf(__builtin_fmaxf(v[5], v[6]), v[7]));
 }
 
 // ---------------------------------------------------------------------------
@@ -106,71 +172,86 @@ struct GroupParams {
 template <int BITS>
 __device__ __forceinline__ GroupParams group_params(float mn, float mx) {
     constexpr float Q = float((1 << BITS) - 1);
+    constexpr float RQ = 1.0f / Q;   // binary32 nearest to 1/Q
     mn = mn + 0.0f;                  // a zero minimum or maximum is taken as +0
     mx = mx + 0.0f;
     const float range = mx - mn;
-    const float s32 = range / Q;     // IEEE division (correctly rounded)
-    const _Float16 sh = (_Float16)s32;   // round to nearest even, gradual underflow
-    const _Float16 zh = (_Float16)mn;
+    // fp32(range / Q) without a division: q0 = range * RQ is within an ulp of
+    // the quotient, so the remainder range - q0*Q is exact in one fma, and one
+    // correction step q0 + rem*RQ rounds to the correctly rounded quotient.
+    // Checked exhaustively against IEEE division over every non-negative
+    // finite binary32 range, for Q = 15 and Q = 255 (denormals preserved).
+    const float q0 = range * RQ;
+    const float rem = __builtin_fmaf(-q0, Q, range);
+    const float s32 = __builtin_fmaf(rem, RQ, q0);
+    const _Float16 sh = (_Float16)as_f32(s32);   // round to nearest even, gradual underflow
+    const _Float16 zh = (_Float16)as_f32(mn);
     const float s = (float)sh;
+    // fp32(1 / s) for an fp16 scale: v_rcp_f32 is within 1 ulp, one Newton
+    // step in fma form leaves a relative error below 2^-44, and 1/s for an
+    // 11-bit significand is never closer than 2^-12 ulp to a rounding
+    // midpoint, so the final fma rounds exactly as IEEE division would
+    // (also checked on the GPU for every positive fp16 scale).
+    const float r0 = __builtin_amdgcn_rcpf(s);
+    const float e = __builtin_fmaf(-s, r0, 1.0f);
     GroupParams p;
     p.z = (float)zh;
-    p.inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+    p.inv = (s == 0.0f) ? 0.0f : __builtin_fmaf(e, r0, r0);
     p.s16 = __builtin_bit_cast(uint16_t, sh);
     p.z16 = __builtin_bit_cast(uint16_t, zh);
     return p;
 }
 
-// clamp(round_half_even(fp32(fp32(v - z) * inv)), 0, Q): after the clamp,
-// adding 1.5 * 2^23 rounds to an integer half to even and leaves that integer
-// in the low mantissa bits, so the code is the low byte of the result.
-template <int BITS>
-__device__ __forceinline__ uint32_t encode(float v, const GroupParams &p) {
-    constexpr float Q = float((1 << BITS) - 1);
-    const float t = (v - p.z) * p.inv;
-    const float c = __builtin_amdgcn_fmed3f(t, 0.0f, Q);
-    return __builtin_bit_cast(uint32_t, c + 12582912.0f);
-}
-
-// Pack the low bytes of four words.
-__device__ __forceinline__ uint32_t pack_lo_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-    const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);   // [a.b0, b.b0, 0, 0]
-    const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x04000C0Cu);   // [0, 0, c.b0, d.b0]
-    return lo | hi;
-}
-
-// Encode the lane's 8 values; 4-bit codes: one word, element 2i in the low
-// nibble of byte i; 8-bit codes: two words, element i in byte i.
+// Codes of the lane's 8 values: q = clamp(round_half_even(fp32(fp32(v - z) *
+// inv)), 0, Q). v_cvt_pk_u8_f32 rounds to nearest even and saturates to
+// [0, 255] while inserting the byte (checked on the GPU), so 8-bit codes need
+// no separate clamp; 4-bit codes are clamped to [0, 15] first (v_med3_f32).
+// Layout: 4-bit codes in one word, element 2i in the low nibble of byte i;
+// 8-bit codes in two words, element i in byte i.
 template <int BITS>
 __device__ __forceinline__ void encode8(const float (&v)[kLaneElems], const GroupParams &p,
                                         uint32_t (&w)[BITS == 4 ? 1 : 2]) {
-    uint32_t e[kLaneElems];
+    float t[kLaneElems];
 #pragma unroll
-    for (int i = 0; i < kLaneElems; ++i) e[i] = encode<BITS>(v[i], p);
+    for (int i = 0; i < kLaneElems; ++i) t[i] = (v[i] - p.z) * p.inv;
     if constexpr (BITS == 8) {
-        w[0] = pack_lo_bytes(e[0], e[1], e[2], e[3]);
-        w[1] = pack_lo_bytes(e[4], e[5], e[6], e[7]);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            uint32_t a = __builtin_amdgcn_cvt_pk_u8_f32(t[4 * k + 0], 0, 0u);
+            a = __builtin_amdgcn_cvt_pk_u8_f32(t[4 * k + 1], 1, a);
+            a = __builtin_amdgcn_cvt_pk_u8_f32(t[4 * k + 2], 2, a);
+            w[k] = __builtin_amdgcn_cvt_pk_u8_f32(t[4 * k + 3], 3, a);
+        }
     } else {
-        // low byte of (e_odd << 4) | e_even is the two nibbles (codes < 16)
-        w[0] = pack_lo_bytes((e[1] << 4) | e[0], (e[3] << 4) | e[2], (e[5] << 4) | e[4],
-                             (e[7] << 4) | e[6]);
+#pragma unroll
+        for (int i = 0; i < kLaneElems; ++i) t[i] = __builtin_amdgcn_fmed3f(t[i], 0.0f, 15.0f);
+        uint32_t ev = __builtin_amdgcn_cvt_pk_u8_f32(t[0], 0, 0u);   // even elements
+        ev = __builtin_amdgcn_cvt_pk_u8_f32(t[2], 1, ev);
+        ev = __builtin_amdgcn_cvt_pk_u8_f32(t[4], 2, ev);
+        ev = __builtin_amdgcn_cvt_pk_u8_f32(t[6], 3, ev);
+        uint32_t od = __builtin_amdgcn_cvt_pk_u8_f32(t[1], 0, 0u);   // odd elements
+        od = __builtin_amdgcn_cvt_pk_u8_f32(t[3], 1, od);
+        od = __builtin_amdgcn_cvt_pk_u8_f32(t[5], 2, od);
+        od = __builtin_amdgcn_cvt_pk_u8_f32(t[7], 3, od);
+        w[0] = ev | (od << 4);
     }
 }
 
-// Unpack 8 codes to binary32 integers.
+// Unpack 8 codes to binary32 integers (v_cvt_f32_ubyte0..3).
 template <int BITS>
 __device__ __forceinline__ void decode8(const uint32_t (&w)[BITS == 4 ? 1 : 2], float (&q)[kLaneElems]) {
     if constexpr (BITS == 8) {
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            q[4 * k + 0] = (float)(w[k] & 0xFFu);
-            q[4 * k + 1] = (float)((w[k] >> 8) & 0xFFu);
-            q[4 * k + 2] = (float)((w[k] >> 16) & 0xFFu);
-            q[4 * k + 3] = (float)(w[k] >> 24);
+            const uint32_t b = w[k];
+            q[4 * k + 0] = (float)(b & 0xFFu);
+            q[4 * k + 1] = (float)((b >> 8) & 0xFFu);
+            q[4 * k + 2] = (float)((b >> 16) & 0xFFu);
+            q[4 * k + 3] = (float)(b >> 24);
         }
     } else {
-        const uint32_t lo = w[0] & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6
-        const uint32_t hi = (w[0] >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
+        const uint32_t lo = opaque(w[0] & 0x0F0F0F0Fu);          // elements 0, 2, 4, 6
+        const uint32_t hi = opaque((w[0] >> 4) & 0x0F0F0F0Fu);   // elements 1, 3, 5, 7
         q[0] = (float)(lo & 0xFFu);
         q[2] = (float)((lo >> 8) & 0xFFu);
         q[4] = (float)((lo >> 16) & 0xFFu);
@@ -182,35 +263,13 @@ __device__ __forceinline__ void decode8(const uint32_t (&w)[BITS == 4 ? 1 : 2], 
     }
 }
 
-template <int BITS>
-__device__ __forceinline__ void load_codes(const uint8_t *__restrict__ codes, uint64_t elem,
-                                           uint32_t (&w)[BITS == 4 ? 1 : 2]) {
-    if constexpr (BITS == 8) {
-        const uint2 v = *reinterpret_cast<const uint2 *>(codes + elem);
-        w[0] = v.x;
-        w[1] = v.y;
-    } else {
-        w[0] = *reinterpret_cast<const uint32_t *>(codes + elem / 2);
-    }
-}
-
-template <int BITS>
-__device__ __forceinline__ void store_codes(uint8_t *__restrict__ codes, uint64_t elem,
-                                            const uint32_t (&w)[BITS == 4 ? 1 : 2]) {
-    if constexpr (BITS == 8) {
-        *reinterpret_cast<uint2 *>(codes + elem) = make_uint2(w[0], w[1]);
-    } else {
-        *reinterpret_cast<uint32_t *>(codes + elem / 2) = w[0];
-    }
-}
-
 __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
     return (float)__builtin_bit_cast(_Float16, b);
 }
 
 // 8 packed 16-bit activations -> binary32 (exact).
 template <int DT>
-__device__ __forceinline__ void widen8(const uint4 &raw, float (&v)[kLaneElems]) {
+__device__ __forceinline__ void widen8(const u32x4 &raw, float (&v)[kLaneElems]) {
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -225,20 +284,22 @@ __device__ __forceinline__ void widen8(const uint4 &raw, float (&v)[kLaneElems])
     }
 }
 
-// binary32 -> 8 packed 16-bit outputs, round to nearest even.
+// binary32 -> 8 packed 16-bit outputs, round to nearest even
+// (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32).
 template <int DT>
-__device__ __forceinline__ uint4 narrow8(const float (&o)[kLaneElems]) {
+__device__ __forceinline__ u32x4 narrow8(const float (&o)[kLaneElems]) {
     uint32_t w[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const f32x2 pair = {o[2 * k], o[2 * k + 1]};
+        const f32x2 pair = {as_f32(o[2 * k]), as_f32(o[2 * k + 1])};
         if constexpr (DT == 1) {
             w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pair, bf16x2));
         } else {
             w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pair, f16x2));
         }
     }
-    return make_uint4(w[0], w[1], w[2], w[3]);
+    const u32x4 r = {w[0], w[1], w[2], w[3]};
+    return r;
 }
 
 }  // namespace fc
