@@ -37,8 +37,8 @@ __global__ __launch_bounds__(kBlockThreads) void dsr_kernel(
     static_assert(U % S == 0 && (U * kSlotElems) % G2 == 0, "a tile holds whole groups");
     const int R = RT > 0 ? RT : R_arg;
 
-    const int lane = threadIdx.x & (kWave - 1);
-    const uint64_t wave = (uint64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+    const int lane = lane_id();
+    const uint64_t wave = wave_index();
     const uint64_t tile = wave * (uint64_t)(U * kSlotElems);
     if (tile >= n) return;
     const uint64_t left = n - tile;

@@ -18,8 +18,8 @@ __global__ __launch_bounds__(kBlockThreads) void dequant_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ s,
     const uint16_t *__restrict__ z, uint64_t n, int g_shift, uint16_t *__restrict__ out) {
     constexpr int W = BITS == 4 ? 1 : 2;
-    const int lane = threadIdx.x & (kWave - 1);
-    const uint64_t wave = (uint64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+    const int lane = lane_id();
+    const uint64_t wave = wave_index();
     const uint64_t tile = wave * (uint64_t)(kSlots * kSlotElems);
     if (tile >= n) return;
     const uint64_t left = n - tile;

@@ -43,6 +43,20 @@ constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v >> 1); }
 // whole number of groups.
 constexpr int tile_slots(int G, int base) { return G > base * kSlotElems ? G / kSlotElems : base; }
 
+// Lane and wave indices from the hardware registers. The wave index is made
+// wave-uniform (SGPR) with readfirstlane: workitem_id / 64 is the same for
+// every lane of a wave, but the compiler cannot know it, and every base
+// address derived from a per-lane value would be computed in 64-bit VGPR
+// arithmetic. (The builtins also avoid the device-library calls behind
+// threadIdx/blockIdx, which are not inlined into code built with the IEEE
+// mode bit off.)
+__device__ __forceinline__ int lane_id() { return (int)(__builtin_amdgcn_workitem_id_x() & (kWave - 1)); }
+
+__device__ __forceinline__ uint64_t wave_index() {
+    const uint32_t w = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_workitem_id_x() / kWave);
+    return (uint64_t)__builtin_amdgcn_workgroup_id_x() * kWavesPerBlock + w;
+}
+
 // Hides a value from the optimizer (no instruction is emitted).
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     asm("" : "+v"(v));

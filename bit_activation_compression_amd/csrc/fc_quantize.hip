@@ -29,8 +29,8 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_kernel(
     constexpr int W = BITS == 4 ? 1 : 2;
     static_assert(U % S == 0 && (U * kSlotElems) % G == 0, "a tile holds whole groups");
 
-    const int lane = threadIdx.x & (kWave - 1);
-    const uint64_t wave = (uint64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+    const int lane = lane_id();
+    const uint64_t wave = wave_index();
     const uint64_t tile = wave * (uint64_t)(U * kSlotElems);
     if (tile >= n) return;
     // Wave-uniform bases; tiles start on a group boundary.
