@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kBlockThreads) void dequant_kernel(
         const float zf = half_bits_to_float(zv[u]);
 #pragma unroll
         for (int k = 0; k < kLaneElems; ++k) o[k] = __builtin_fmaf(q[k], sf, zf);   // exact product
-        stv<u32x4, false>(ob, rel * 2, narrow8<DT>(o));
+        stv<u32x4, true>(ob, rel * 2, narrow8<DT>(o));   // streamed out, not re-read
     }
 }
 

@@ -15,9 +15,10 @@
 namespace fc {
 namespace {
 
-// Tiles of 8 slots (16 KiB of input per wave) with non-temporal loads and
-// code stores measured fastest on MI355X for this read-4 / write-1 stream.
-constexpr int kTileSlots = 8;
+// Tiles of 4 slots (8 KiB of input per wave) with non-temporal loads and
+// code stores measured fastest on MI355X for this read-4 / write-1 stream,
+// counting the effect on the kernel that reads the codes next.
+constexpr int kTileSlots = 4;
 
 template <int DT, int BITS, int G>
 __global__ __launch_bounds__(kBlockThreads) void quantize_kernel(
