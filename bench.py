@@ -52,6 +52,17 @@ def model_bytes(R: int, T: int, H: int, bits: int, group: int, group2: int, e: i
     return {"k1": k1, "k2": k2, "k3": k3, "total": k1 + k2 + k3, "payload1": p1, "payload2": p2}
 
 
+def link_bytes(R: int, T: int, H: int, bits: int, group: int, group2: int, e: int = 2) -> dict:
+    """Bytes one rank would send over the links for one all-reduce of a [T][H] tensor: a ring
+    all-reduce of 16-bit values (2(R-1) hops of 1/R of the tensor) vs the two-step codec
+    (reduce-scatter of its payload-1 chunks, all-gather of its payload-2 chunk)."""
+    ring = 2 * (R - 1) * T * H * e // R
+    rs = (R - 1) * (T * (H // R) * bits // 8 + T * (H // R) // min(group, H // R) * 4) if group <= H // R \
+        else (R - 1) * (T * (H // R) * bits // 8 + T * (H // group) * 4)
+    ag = (R - 1) * (T * (H // R) * bits // 8 + T * (H // R) // group2 * 4)
+    return {"ring_16bit": ring, "two_step_codec": rs + ag, "ratio": round(ring / (rs + ag), 3)}
+
+
 def k1_source_hash() -> str:
     h = hashlib.sha256()
     for rel in K1_SOURCES:
@@ -197,6 +208,28 @@ def main() -> int:
     copy_gbps = 2 * (1 << 30) * 10 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
     del src, dst
 
+    # The uncompressed all-reduce result on the same operands: the arithmetic of
+    # the ring all-reduce the method replaces, as an on-GPU comparator.
+    xd0 = sets[0][0]
+    sum_out = torch.empty((T, H), dtype=tdt, device=dev)
+    for _ in range(5):
+        fc.fc_sum_uncompressed(xd0, sum_out, stream=stream)
+    se = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    se[0].record(stream)
+    for _ in range(50):
+        fc.fc_sum_uncompressed(xd0, sum_out, stream=stream)
+    se[1].record(stream)
+    torch.cuda.synchronize()
+    sum_ms = se[0].elapsed_time(se[1]) / 50
+    sum_bytes = (R + 1) * T * H * 2
+    # codec output vs the uncompressed result (diagnostic, in torch on the GPU)
+    step(0)
+    torch.cuda.synchronize()
+    diff = sets[0][7].float() - sum_out.float()
+    mse = float((diff * diff).mean())
+    ref_pow = float((sum_out.float() ** 2).mean())
+    del diff
+
     value = mb["total"] / (ms_per_step * 1e-3) / 1e9
     k1_avg_ms = float(k1_ms.mean())
     k1_gbps = mb["k1"] / (k1_avg_ms * 1e-3) / 1e9
@@ -246,6 +279,11 @@ def main() -> int:
                         "k3_dequantize": round(mb["k3"] / (k_avg[2] * 1e-3) / 1e9, 1)},
         "pipeline_ms_median_events": round(float(np.median(pipe_ms)), 5),
         "copy_ceiling_gbps": round(copy_gbps, 1),
+        "uncompressed_sum": {"ms": round(sum_ms, 5), "bytes": sum_bytes,
+                             "gbps": round(sum_bytes / (sum_ms * 1e-3) / 1e9, 1),
+                             "codec_mse_vs_uncompressed": mse,
+                             "codec_snr_db": round(10 * np.log10(ref_pow / mse), 2) if mse > 0 else None},
+        "link_bytes_per_rank": link_bytes(R, T, H, bits, group, g2),
         "roofline": {"bound": "hbm", "kernel": "k1_quantize", "achieved": round(k1_gbps, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(k1_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": mb["k1"],

@@ -24,7 +24,7 @@ __all__ = [
     "FcError", "lib", "library_path",
     "fc_quantize_groups", "fc_dequant_sum_requant", "fc_dequantize", "fc_allreduce_emulated",
     "fc_workspace_bytes", "fc_workspace_layout", "fc_stage2_group", "fc_status_string",
-    "workspace_views", "EXPORTED_SYMBOLS",
+    "fc_sum_uncompressed", "workspace_views", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -35,6 +35,7 @@ _DTYPES = {torch.float16: FC_F16, torch.bfloat16: FC_BF16}
 EXPORTED_SYMBOLS = (
     "fc_quantize_groups", "fc_dequant_sum_requant", "fc_dequantize", "fc_allreduce_emulated",
     "fc_workspace_bytes", "fc_workspace_layout", "fc_stage2_group", "fc_status_string",
+    "fc_sum_uncompressed",
 )
 
 _lock = threading.Lock()
@@ -62,8 +63,9 @@ def lib() -> ctypes.CDLL:
             L.fc_dequant_sum_requant.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P]
             L.fc_dequantize.argtypes = [P, P, P, I, I, I, I, I, P, P]
             L.fc_allreduce_emulated.argtypes = [P, I, I, I, I, I, I, P, P, Z, P]
+            L.fc_sum_uncompressed.argtypes = [P, I, I, I, I, P, P]
             for f in (L.fc_quantize_groups, L.fc_dequant_sum_requant, L.fc_dequantize,
-                      L.fc_allreduce_emulated):
+                      L.fc_allreduce_emulated, L.fc_sum_uncompressed):
                 f.restype = I
             L.fc_workspace_bytes.argtypes = [I, I, I, I, I]
             L.fc_workspace_bytes.restype = Z
@@ -183,6 +185,17 @@ def fc_allreduce_emulated(x: torch.Tensor, bits: int, group: int, out=None, work
                                        _ptr(workspace), workspace.numel(), _stream(stream, dev)),
            "fc_allreduce_emulated")
     return out, workspace
+
+
+def fc_sum_uncompressed(x: torch.Tensor, out=None, stream=None):
+    """x [R, T, H] fp16/bf16 -> out [T, H]: the uncompressed all-reduce result (binary32 sum)."""
+    _dev_tensor(x, "x")
+    R, T, H = x.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=x.device)
+    _check(lib().fc_sum_uncompressed(_ptr(x), _DTYPES[x.dtype], R, T, H, _ptr(out),
+                                     _stream(stream, x.device)), "fc_sum_uncompressed")
+    return out
 
 
 def workspace_views(workspace: torch.Tensor, R: int, T: int, H: int, bits: int, group: int) -> dict:

@@ -141,6 +141,17 @@ fc_status fc_allreduce_emulated(const void *x, fc_dtype dt, int R, int T, int H,
                                           static_cast<uint16_t *>(out), s));
 }
 
+fc_status fc_sum_uncompressed(const void *x, fc_dtype dt, int R, int T, int H, void *out,
+                              void *stream) {
+    if (R < 1 || T < 0 || H < 1 || H % 8 != 0) return FC_ERR_SHAPE;
+    if (dt != FC_F16 && dt != FC_BF16) return FC_ERR_DTYPE;
+    const uint64_t n = (uint64_t)T * (uint64_t)H;
+    fc_status st = check_ptrs(n, {x, out});
+    if (st != FC_OK || n == 0) return st;
+    return from_hip(fc::launch_sum(static_cast<const uint16_t *>(x), (int)dt, R, n,
+                                   static_cast<uint16_t *>(out), static_cast<hipStream_t>(stream)));
+}
+
 size_t fc_workspace_bytes(int R, int T, int H, int bits, int group) {
     int g2 = 0;
     if (check_shape(R, T, H, bits, group, &g2) != FC_OK) return 0;

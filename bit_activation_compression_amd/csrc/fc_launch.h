@@ -24,4 +24,8 @@ hipError_t launch_dequantize(const uint8_t *codes2, const uint16_t *s2, const ui
                              uint64_t n, int bits, int group2, int dtype, uint16_t *out,
                              hipStream_t stream);
 
+// Uncompressed R-way sum over n = T*H positions of R operands laid out [R][n].
+hipError_t launch_sum(const uint16_t *x, int dtype, int R, uint64_t n, uint16_t *out,
+                      hipStream_t stream);
+
 }  // namespace fc

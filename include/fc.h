@@ -110,6 +110,19 @@ fc_status fc_dequantize(const uint8_t *codes2, const uint16_t *s2, const uint16_
 fc_status fc_allreduce_emulated(const void *x, fc_dtype dt, int R, int T, int H, int bits, int group,
                                 void *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * The uncompressed all-reduce result the page compares against (Figure 1: an
+ * NCCL Ring All-Reduce of FP16 activations), computed on one GPU as the
+ * reference point for the codec's speed and error:
+ *   out[t][h] = round_half_even_to_dt(x[0][t][h] + x[1][t][h] + ... )
+ * summed in binary32 in ascending r from operand 0 and rounded once (a ring
+ * in the 16-bit type would round after every hop instead).
+ *   x [R][T][H] in dt -> out [T][H] in dt. Requires R >= 1, T >= 0 and
+ *   H % 8 == 0 (FC_ERR_SHAPE otherwise).
+ */
+fc_status fc_sum_uncompressed(const void *x, fc_dtype dt, int R, int T, int H, void *out,
+                              void *stream);
+
 /* Bytes of workspace fc_allreduce_emulated needs; 0 if the arguments are unsupported. */
 size_t fc_workspace_bytes(int R, int T, int H, int bits, int group);
 

@@ -23,7 +23,7 @@ __all__ = [
     "build", "lib", "F16", "BF16", "OracleError",
     "half_to_float", "float_to_half", "bf16_to_float", "float_to_bf16",
     "quantize_groups", "dequant_sum_requant", "dequantize", "quantize_f32",
-    "allreduce", "stage2_group", "code_bytes",
+    "allreduce", "stage2_group", "code_bytes", "sum_uncompressed",
 ]
 
 F16 = "f16"
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
             L.ref_dequantize.argtypes = [P, P, P, I, I, I, I, I, P, P]
             L.ref_quantize_f32.restype = I
             L.ref_quantize_f32.argtypes = [P, ctypes.c_size_t, I, I, P, P, P]
+            L.ref_sum_uncompressed.restype = I
+            L.ref_sum_uncompressed.argtypes = [P, I, I, I, I, P]
             for name in ("ref_half_to_float_n", "ref_bf16_to_float_n",
                          "ref_float_to_half_n", "ref_float_to_bf16_n"):
                 fn = getattr(L, name)
@@ -205,3 +207,12 @@ def allreduce(x: np.ndarray, dtype: str, bits: int, group: int, want_f32: bool =
     out, o32 = dequantize(codes2, s2, z2, T, H, bits, g2, dtype, want_o32=want_f32)
     return dict(codes1=codes1, s1=s1, z1=z1, codes2=codes2, s2=s2, z2=z2, y=y, o32=o32,
                 out=out, group2=g2)
+
+
+def sum_uncompressed(x: np.ndarray, dtype: str) -> np.ndarray:
+    """The uncompressed all-reduce: out [T, H] = 16-bit rounding of the binary32 sum over r."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    R, T, H = x.shape
+    out = np.zeros((T, H), dtype=np.uint16)
+    _check(lib().ref_sum_uncompressed(_p(x), _DT[dtype], R, T, H, _p(out)), "sum_uncompressed")
+    return out

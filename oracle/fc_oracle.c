@@ -419,3 +419,28 @@ void ref_float_to_bf16_n(const float *f, uint16_t *b, size_t n)
     for (size_t i = 0; i < n; ++i)
         b[i] = ref_float_to_bf16(f[i]);
 }
+
+/*
+ * The uncompressed all-reduce the page compares against (Figure 1: an NCCL
+ * Ring All-Reduce of FP16 activations): every rank ends with the sum of the
+ * R operands. Reading taken here: binary32 accumulation in ascending operand
+ * order, starting from operand 0, rounded once to the 16-bit dtype (a ring
+ * in the 16-bit type would round after every hop instead).
+ *   x [R][T][H] 16-bit -> out [T][H] 16-bit
+ */
+int ref_sum_uncompressed(const uint16_t *x, int dtype, int R, int T, int H, uint16_t *out)
+{
+    if (R < 1 || T < 0 || H < 1)
+        return REF_ERR_SHAPE;
+    for (int t = 0; t < T; ++t) {
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int r = 0; r < R; ++r) {
+                float v = widen(x[((size_t)r * T + t) * H + h], dtype);
+                acc = (r == 0) ? v : acc + v;
+            }
+            out[(size_t)t * H + h] = narrow(acc, dtype);
+        }
+    }
+    return REF_OK;
+}

@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     L = fc.lib()
     names = _declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     for n in names:
         assert hasattr(L, n), n
     assert sorted(names) == sorted(fc.EXPORTED_SYMBOLS)
@@ -104,3 +104,8 @@ def test_other_entry_points_validate():
     assert L.fc_allreduce_emulated(FAKE, 0, 2, 8, 256, 8, 128, FAKE, FAKE, need - 1, None) == 5
     assert L.fc_allreduce_emulated(FAKE, 0, 2, 8, 256, 8, 128, None, FAKE, need, None) == 1
     assert L.fc_allreduce_emulated(None, 0, 2, 0, 256, 8, 128, None, None, 0, None) == 0
+    assert L.fc_sum_uncompressed(FAKE, 0, 0, 8, 256, FAKE, None) == 2
+    assert L.fc_sum_uncompressed(FAKE, 0, 2, 8, 250, FAKE, None) == 2
+    assert L.fc_sum_uncompressed(FAKE, 3, 2, 8, 256, FAKE, None) == 7
+    assert L.fc_sum_uncompressed(MISALIGNED, 0, 2, 8, 256, FAKE, None) == 4
+    assert L.fc_sum_uncompressed(None, 0, 2, 0, 256, None, None) == 0

@@ -486,3 +486,42 @@ def test_empty_token_dimension():
     x = np.zeros((2, 0, 64), dtype=np.uint16)
     res = oracle.allreduce(x, oracle.F16, 4, 16)
     assert res["out"].shape == (0, 64)
+
+
+# ---------------------------------------------------------------------------
+# the uncompressed comparator (the ring all-reduce's result)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [oracle.F16, oracle.BF16])
+def test_uncompressed_sum_exact_for_dyadic_operands(dtype):
+    """Quarter-integers in [-8, 8]: every partial sum is exact in binary32 and the total fits
+    the 16-bit type, so the result is the exact sum (closed form)."""
+    rng = np.random.default_rng(21)
+    x = rng.integers(-32, 33, size=(4, 5, 64)) / 4.0
+    out = oracle.sum_uncompressed(synth.operands_from_values(x, dtype), dtype)
+    assert np.array_equal(_widen(out, dtype), x.sum(axis=0))
+
+
+def test_uncompressed_sum_is_rounded_exact_sum_for_two_operands():
+    """R = 2: the binary32 sum of two fp16 values is within 2^-24 (relative) of the exact sum,
+    so rounding it to fp16 gives numpy's float16 rounding of the fp64 sum unless the binary32
+    rounding lands exactly on an fp16 midpoint (this data has no such case); swapping the
+    operands changes nothing."""
+    rng = np.random.default_rng(22)
+    x = (rng.standard_normal((2, 16, 256)) * 4).astype(np.float16)
+    xb = x.view(np.uint16)
+    out = oracle.sum_uncompressed(xb, oracle.F16)
+    exact = x.astype(np.float64).sum(axis=0)
+    assert np.array_equal(out, exact.astype(np.float16).view(np.uint16))
+    assert np.array_equal(out, oracle.sum_uncompressed(xb[::-1].copy(), oracle.F16))
+
+
+def test_uncompressed_sum_error_bound():
+    """|out - sum| <= (R-1) * 2^-24 * sum|x| + half a 16-bit ulp (sequential binary32 sum, one rounding)."""
+    w = _small("llama3_70b_prefill", T=8)
+    x = synth.operands(w, 4)
+    out = _widen(oracle.sum_uncompressed(x, w.dtype), w.dtype)
+    xv = _widen(x, w.dtype)
+    exact = xv.sum(axis=0)
+    bound = (w.R - 1) * 2.0 ** -24 * np.abs(xv).sum(axis=0) + np.abs(exact) * 2.0 ** -8 + 2.0 ** -133
+    assert np.all(np.abs(out - exact) <= bound)
