@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
             L.ref_quantize_groups.argtypes = [P, I, I, I, I, I, I, P, P, P]
             L.ref_dequant_sum_requant.restype = I
             L.ref_dequant_sum_requant.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P]
+            L.ref_dequant_sum_requant_mixed.restype = I
+            L.ref_dequant_sum_requant_mixed.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P]
             L.ref_dequantize.restype = I
             L.ref_dequantize.argtypes = [P, P, P, I, I, I, I, I, P, P]
             L.ref_quantize_f32.restype = I
@@ -157,20 +159,23 @@ def quantize_groups(x: np.ndarray, dtype: str, bits: int, group: int):
 
 
 def dequant_sum_requant(codes1, s1, z1, R: int, T: int, H: int, bits: int, group: int,
-                        want_y: bool = False):
-    """Stage-1 payload -> (codes2 [T, H*bits/8], s2, z2 [T, H/g2], y [T, H] f32 or None)."""
+                        want_y: bool = False, bits2: int | None = None):
+    """Stage-1 payload -> (codes2 [T, H*bits2/8], s2, z2 [T, H/g2], y [T, H] f32 or None).
+    `bits` is the stage-1 code width, `bits2` (default: the same) the stage-2 one."""
+    bits2 = bits if bits2 is None else bits2
     g2 = stage2_group(R, H, group)
     if g2 <= 0 or H % g2:
         raise OracleError(2, "dequant_sum_requant")
     codes1 = np.ascontiguousarray(codes1, dtype=np.uint8)
     s1 = np.ascontiguousarray(s1, dtype=np.uint16)
     z1 = np.ascontiguousarray(z1, dtype=np.uint16)
-    codes2 = np.zeros((T, code_bytes(H, bits)), dtype=np.uint8)
+    codes2 = np.zeros((T, code_bytes(H, bits2)), dtype=np.uint8)
     s2 = np.zeros((T, H // g2), dtype=np.uint16)
     z2 = np.zeros_like(s2)
     y = np.zeros((T, H), dtype=np.float32) if want_y else None
-    _check(lib().ref_dequant_sum_requant(_p(codes1), _p(s1), _p(z1), R, T, H, bits, group,
-                                         _p(codes2), _p(s2), _p(z2), _p(y)), "dequant_sum_requant")
+    _check(lib().ref_dequant_sum_requant_mixed(_p(codes1), _p(s1), _p(z1), R, T, H, bits, bits2,
+                                               group, _p(codes2), _p(s2), _p(z2), _p(y)),
+           "dequant_sum_requant")
     return codes2, s2, z2, y
 
 
@@ -198,13 +203,17 @@ def quantize_f32(v: np.ndarray, bits: int, group: int):
     return codes, s, z
 
 
-def allreduce(x: np.ndarray, dtype: str, bits: int, group: int, want_f32: bool = True) -> dict:
-    """The whole path on one host: every intermediate of the emulated all-reduce."""
+def allreduce(x: np.ndarray, dtype: str, bits: int, group: int, want_f32: bool = True,
+              bits2: int | None = None) -> dict:
+    """The whole path on one host: every intermediate of the emulated all-reduce.
+    `bits` codes the reduce-scatter payload, `bits2` (default: the same) the all-gather one."""
+    bits2 = bits if bits2 is None else bits2
     R, T, H = x.shape
     codes1, s1, z1 = quantize_groups(x, dtype, bits, group)
-    codes2, s2, z2, y = dequant_sum_requant(codes1, s1, z1, R, T, H, bits, group, want_y=want_f32)
+    codes2, s2, z2, y = dequant_sum_requant(codes1, s1, z1, R, T, H, bits, group, want_y=want_f32,
+                                            bits2=bits2)
     g2 = stage2_group(R, H, group)
-    out, o32 = dequantize(codes2, s2, z2, T, H, bits, g2, dtype, want_o32=want_f32)
+    out, o32 = dequantize(codes2, s2, z2, T, H, bits2, g2, dtype, want_o32=want_f32)
     return dict(codes1=codes1, s1=s1, z1=z1, codes2=codes2, s2=s2, z2=z2, y=y, o32=o32,
                 out=out, group2=g2)
 

@@ -290,14 +290,19 @@ done:
  * and each chunk reads the same group metadata) and sums them in binary32 in
  * ascending r, starting from operand 0. The sum is requantized in groups of
  * g2 = min(group, C) columns, which never cross a chunk.
- *   codes2 [T][H*bits/8], s2, z2 [T][H/g2]
+ * bits1 is the width of the incoming (stage-1) codes, bits2 the width of the
+ * requantized (stage-2) codes; the page quantizes before both steps and does
+ * not say they must be equal.
+ *   codes2 [T][H*bits2/8], s2, z2 [T][H/g2]
  *   y      [T][H] binary32 sums (optional, may be NULL)
  */
-int ref_dequant_sum_requant(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1,
-                            int R, int T, int H, int bits, int group,
-                            uint8_t *codes2, uint16_t *s2, uint16_t *z2, float *y_out)
+int ref_dequant_sum_requant_mixed(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1,
+                                  int R, int T, int H, int bits1, int bits2, int group,
+                                  uint8_t *codes2, uint16_t *s2, uint16_t *z2, float *y_out)
 {
-    int st = check_args(R, T, H, bits, group);
+    int st = check_args(R, T, H, bits1, group);
+    if (st == REF_OK)
+        st = check_args(R, T, H, bits2, group);
     if (st != REF_OK)
         return st;
     const int C = H / R;
@@ -318,7 +323,7 @@ int ref_dequant_sum_requant(const uint8_t *codes1, const uint16_t *s1, const uin
                 for (int r = 0; r < R; ++r) {
                     size_t row = (size_t)r * T + t;
                     size_t m = row * G1 + (size_t)(h / group);
-                    float xh = dequant(get_code(codes1, row * H + (size_t)h, bits), s1[m], z1[m]);
+                    float xh = dequant(get_code(codes1, row * H + (size_t)h, bits1), s1[m], z1[m]);
                     acc = (r == 0) ? xh : acc + xh;
                 }
                 y[c] = acc;
@@ -328,11 +333,11 @@ int ref_dequant_sum_requant(const uint8_t *codes1, const uint16_t *s1, const uin
             for (int k = 0; k < C / g2; ++k) {
                 int h0 = j * C + k * g2;
                 size_t m = (size_t)t * G2 + (size_t)(h0 / g2);
-                st = quantize_group(y + (size_t)k * g2, (size_t)g2, bits, q, &s2[m], &z2[m]);
+                st = quantize_group(y + (size_t)k * g2, (size_t)g2, bits2, q, &s2[m], &z2[m]);
                 if (st != REF_OK)
                     goto done;
                 for (int i = 0; i < g2; ++i)
-                    put_code(codes2, (size_t)t * H + (size_t)h0 + i, bits, q[i]);
+                    put_code(codes2, (size_t)t * H + (size_t)h0 + i, bits2, q[i]);
             }
         }
     }
@@ -340,6 +345,15 @@ done:
     free(y);
     free(q);
     return st;
+}
+
+/* Same code width before both steps. */
+int ref_dequant_sum_requant(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1,
+                            int R, int T, int H, int bits, int group,
+                            uint8_t *codes2, uint16_t *s2, uint16_t *z2, float *y_out)
+{
+    return ref_dequant_sum_requant_mixed(codes1, s1, z1, R, T, H, bits, bits, group, codes2, s2, z2,
+                                         y_out);
 }
 
 /*

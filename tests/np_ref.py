@@ -71,7 +71,8 @@ def dequant(q: np.ndarray, s_bits: np.ndarray, z_bits: np.ndarray) -> np.ndarray
     return q.astype(np.float32) * s[..., None] + z[..., None]
 
 
-def allreduce(x: np.ndarray, dtype: str, bits: int, group: int) -> dict:
+def allreduce(x: np.ndarray, dtype: str, bits: int, group: int, bits2: int | None = None) -> dict:
+    bits2 = bits if bits2 is None else bits2
     R, T, H = x.shape
     C = H // R
     g2 = min(group, C)
@@ -81,9 +82,9 @@ def allreduce(x: np.ndarray, dtype: str, bits: int, group: int) -> dict:
     y = xh[0].copy()
     for r in range(1, R):
         y = y + xh[r]
-    q2, s2, z2 = quantize(y.reshape(T, H // g2, g2), bits)
+    q2, s2, z2 = quantize(y.reshape(T, H // g2, g2), bits2)
     o32 = dequant(q2, s2, z2).reshape(T, H)
     return dict(
         codes1=pack(q1.reshape(R * T, H), bits).reshape(R, T, -1), s1=s1, z1=z1,
-        codes2=pack(q2.reshape(T, H), bits), s2=s2, z2=z2, y=y, o32=o32,
+        codes2=pack(q2.reshape(T, H), bits2), s2=s2, z2=z2, y=y, o32=o32,
         out=narrow(o32, dtype), group2=g2)

@@ -35,3 +35,15 @@ def test_odd_shapes(R, H, g):
     b = np_allreduce(x, w.dtype, w.bits, w.group)
     for k in ("codes1", "s1", "z1", "codes2", "s2", "z2", "out"):
         assert np.array_equal(a[k].reshape(-1), b[k].reshape(-1)), k
+
+
+@pytest.mark.parametrize("bits,bits2", [(4, 8), (8, 4)])
+@pytest.mark.parametrize("name", ["llama3_8b_prefill", "llama3_70b_prefill", "decode", "sweep_int4_g4096"])
+def test_mixed_widths_equal_numpy_rederivation(name, bits, bits2):
+    w = synth.workload(name)
+    w = w.with_(T=min(w.T, 16))
+    x = synth.operands(w, 6)
+    a = oracle.allreduce(x, w.dtype, bits, w.group, bits2=bits2)
+    b = np_allreduce(x, w.dtype, bits, w.group, bits2=bits2)
+    for k in ("codes1", "s1", "z1", "codes2", "s2", "z2", "out"):
+        assert np.array_equal(a[k].reshape(-1), b[k].reshape(-1)), (name, k)

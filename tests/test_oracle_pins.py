@@ -525,3 +525,46 @@ def test_uncompressed_sum_error_bound():
     exact = xv.sum(axis=0)
     bound = (w.R - 1) * 2.0 ** -24 * np.abs(xv).sum(axis=0) + np.abs(exact) * 2.0 ** -8 + 2.0 ** -133
     assert np.all(np.abs(out - exact) <= bound)
+
+
+# ---------------------------------------------------------------------------
+# different code widths before the reduce-scatter and before the all-gather
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits,bits2", [(4, 8), (8, 4)])
+def test_mixed_widths_constant_groups_round_trip(bits, bits2):
+    rng = np.random.default_rng(31)
+    R, T, H, g = 4, 3, 256, 32
+    vals = rng.integers(-32, 33, size=(R, T, H // g)) / 4.0
+    x = np.repeat(vals, g, axis=2)
+    res = oracle.allreduce(_f16(x), oracle.F16, bits, g, bits2=bits2)
+    assert res["codes2"].shape == (T, H * bits2 // 8)
+    assert np.array_equal(_hval(res["out"]), x.sum(axis=0))
+
+
+@pytest.mark.parametrize("bits,bits2", [(4, 8), (8, 4)])
+def test_mixed_widths_error_bound(bits, bits2):
+    """|o32 - sum x| <= sum_r s1_r/2 + s2/2 + 2^-10 |sum x| with each stage's own scale."""
+    w = _small("llama3_8b_prefill", T=16)
+    x = synth.operands(w, 8)
+    res = oracle.allreduce(x, w.dtype, bits, w.group, bits2=bits2)
+    exact = _widen(x, w.dtype).sum(axis=0)
+    s1 = np.repeat(_hval(res["s1"]), w.group, axis=2).sum(axis=0)
+    s2 = np.repeat(_hval(res["s2"]), res["group2"], axis=1)
+    tol = s1 / 2 + s2 / 2 + 2.0 ** -10 * np.abs(exact)
+    assert np.all(np.abs(res["o32"].astype(np.float64) - exact) <= tol)
+
+
+def test_mixed_widths_mse_between_uniform_widths():
+    """Figure 5 (right) contrasts the error of quantizing before RS and before AG: 8 bits at
+    either step lowers the end-to-end MSE of all-4-bit codes, and all-8-bit codes are best."""
+    w = _small("llama3_8b_prefill", T=32)
+    x = synth.operands(w, 12)
+    exact = _hval(x).sum(axis=0)
+    mse = {}
+    for b1 in (4, 8):
+        for b2 in (4, 8):
+            o = oracle.allreduce(x, w.dtype, b1, w.group, bits2=b2)["o32"].astype(np.float64)
+            mse[b1, b2] = float(np.mean((o - exact) ** 2))
+    assert mse[4, 4] > mse[4, 8] > mse[8, 8]
+    assert mse[4, 4] > mse[8, 4] > mse[8, 8]
