@@ -35,7 +35,8 @@ _DTYPES = {torch.float16: FC_F16, torch.bfloat16: FC_BF16}
 EXPORTED_SYMBOLS = (
     "fc_quantize_groups", "fc_dequant_sum_requant", "fc_dequantize", "fc_allreduce_emulated",
     "fc_workspace_bytes", "fc_workspace_layout", "fc_stage2_group", "fc_status_string",
-    "fc_sum_uncompressed",
+    "fc_sum_uncompressed", "fc_dequant_sum_requant_mixed", "fc_allreduce_emulated_mixed",
+    "fc_workspace_bytes_mixed", "fc_workspace_layout_mixed",
 )
 
 _lock = threading.Lock()
@@ -64,9 +65,17 @@ def lib() -> ctypes.CDLL:
             L.fc_dequantize.argtypes = [P, P, P, I, I, I, I, I, P, P]
             L.fc_allreduce_emulated.argtypes = [P, I, I, I, I, I, I, P, P, Z, P]
             L.fc_sum_uncompressed.argtypes = [P, I, I, I, I, P, P]
+            L.fc_dequant_sum_requant_mixed.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P]
+            L.fc_allreduce_emulated_mixed.argtypes = [P, I, I, I, I, I, I, I, P, P, Z, P]
             for f in (L.fc_quantize_groups, L.fc_dequant_sum_requant, L.fc_dequantize,
-                      L.fc_allreduce_emulated, L.fc_sum_uncompressed):
+                      L.fc_allreduce_emulated, L.fc_sum_uncompressed,
+                      L.fc_dequant_sum_requant_mixed, L.fc_allreduce_emulated_mixed):
                 f.restype = I
+            L.fc_workspace_bytes_mixed.argtypes = [I, I, I, I, I, I]
+            L.fc_workspace_bytes_mixed.restype = Z
+            L.fc_workspace_layout_mixed.argtypes = [I, I, I, I, I, I, ctypes.POINTER(Z),
+                                                    ctypes.POINTER(Z)]
+            L.fc_workspace_layout_mixed.restype = I
             L.fc_workspace_bytes.argtypes = [I, I, I, I, I]
             L.fc_workspace_bytes.restype = Z
             L.fc_workspace_layout.argtypes = [I, I, I, I, I, ctypes.POINTER(Z), ctypes.POINTER(Z)]
@@ -109,15 +118,22 @@ def fc_stage2_group(R: int, H: int, group: int) -> int:
     return lib().fc_stage2_group(R, H, group)
 
 
-def fc_workspace_bytes(R: int, T: int, H: int, bits: int, group: int) -> int:
-    return lib().fc_workspace_bytes(R, T, H, bits, group)
+def fc_workspace_bytes(R: int, T: int, H: int, bits: int, group: int,
+                       bits2: int | None = None) -> int:
+    if bits2 is None or bits2 == bits:
+        return lib().fc_workspace_bytes(R, T, H, bits, group)
+    return lib().fc_workspace_bytes_mixed(R, T, H, bits, bits2, group)
 
 
-def fc_workspace_layout(R: int, T: int, H: int, bits: int, group: int):
+def fc_workspace_layout(R: int, T: int, H: int, bits: int, group: int, bits2: int | None = None):
     """[(offset, size)] of the six workspace slices: codes1, s1, z1, codes2, s2, z2."""
     off = (ctypes.c_size_t * 6)()
     size = (ctypes.c_size_t * 6)()
-    _check(lib().fc_workspace_layout(R, T, H, bits, group, off, size), "fc_workspace_layout")
+    if bits2 is None or bits2 == bits:
+        _check(lib().fc_workspace_layout(R, T, H, bits, group, off, size), "fc_workspace_layout")
+    else:
+        _check(lib().fc_workspace_layout_mixed(R, T, H, bits, bits2, group, off, size),
+               "fc_workspace_layout_mixed")
     return [(off[i], size[i]) for i in range(6)]
 
 
@@ -139,21 +155,27 @@ def fc_quantize_groups(x: torch.Tensor, bits: int, group: int, codes1=None, s1=N
 
 
 def fc_dequant_sum_requant(codes1, s1, z1, R: int, T: int, H: int, bits: int, group: int,
-                           codes2=None, s2=None, z2=None, stream=None):
-    """Stage-1 payload -> (codes2 [T, H*bits/8], s2, z2 [T, H/g2])."""
+                           codes2=None, s2=None, z2=None, stream=None, bits2: int | None = None):
+    """Stage-1 payload -> (codes2 [T, H*bits2/8], s2, z2 [T, H/g2]); bits2 defaults to bits."""
+    bits2 = bits if bits2 is None else bits2
     for n, t in (("codes1", codes1), ("s1", s1), ("z1", z1)):
         _dev_tensor(t, n)
     dev = codes1.device
     g2 = fc_stage2_group(R, H, group)
     if codes2 is None:
-        codes2 = torch.empty((T, H * bits // 8), dtype=torch.uint8, device=dev)
+        codes2 = torch.empty((T, H * bits2 // 8), dtype=torch.uint8, device=dev)
     if s2 is None:
         s2 = torch.empty((T, H // g2 if g2 else 0), dtype=torch.uint16, device=dev)
     if z2 is None:
         z2 = torch.empty_like(s2)
-    _check(lib().fc_dequant_sum_requant(_ptr(codes1), _ptr(s1), _ptr(z1), R, T, H, bits, group,
-                                        _ptr(codes2), _ptr(s2), _ptr(z2), _stream(stream, dev)),
-           "fc_dequant_sum_requant")
+    if bits2 == bits:
+        st = lib().fc_dequant_sum_requant(_ptr(codes1), _ptr(s1), _ptr(z1), R, T, H, bits, group,
+                                          _ptr(codes2), _ptr(s2), _ptr(z2), _stream(stream, dev))
+    else:
+        st = lib().fc_dequant_sum_requant_mixed(_ptr(codes1), _ptr(s1), _ptr(z1), R, T, H, bits,
+                                                bits2, group, _ptr(codes2), _ptr(s2), _ptr(z2),
+                                                _stream(stream, dev))
+    _check(st, "fc_dequant_sum_requant")
     return codes2, s2, z2
 
 
@@ -171,19 +193,26 @@ def fc_dequantize(codes2, s2, z2, T: int, H: int, bits: int, group2: int, dtype:
 
 
 def fc_allreduce_emulated(x: torch.Tensor, bits: int, group: int, out=None, workspace=None,
-                          stream=None):
-    """x [R, T, H] -> out [T, H]: the whole emulated all-reduce (three kernels)."""
+                          stream=None, bits2: int | None = None):
+    """x [R, T, H] -> out [T, H]: the whole emulated all-reduce (three kernels).
+    `bits` codes the reduce-scatter payload, `bits2` (default: the same) the all-gather one."""
     _dev_tensor(x, "x")
+    bits2 = bits if bits2 is None else bits2
     R, T, H = x.shape
     dev = x.device
     if out is None:
         out = torch.empty((T, H), dtype=x.dtype, device=dev)
     if workspace is None:
-        workspace = torch.empty(max(fc_workspace_bytes(R, T, H, bits, group), 1), dtype=torch.uint8,
-                                device=dev)
-    _check(lib().fc_allreduce_emulated(_ptr(x), _DTYPES[x.dtype], R, T, H, bits, group, _ptr(out),
-                                       _ptr(workspace), workspace.numel(), _stream(stream, dev)),
-           "fc_allreduce_emulated")
+        workspace = torch.empty(max(fc_workspace_bytes(R, T, H, bits, group, bits2), 1),
+                                dtype=torch.uint8, device=dev)
+    if bits2 == bits:
+        st = lib().fc_allreduce_emulated(_ptr(x), _DTYPES[x.dtype], R, T, H, bits, group, _ptr(out),
+                                         _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    else:
+        st = lib().fc_allreduce_emulated_mixed(_ptr(x), _DTYPES[x.dtype], R, T, H, bits, bits2, group,
+                                               _ptr(out), _ptr(workspace), workspace.numel(),
+                                               _stream(stream, dev))
+    _check(st, "fc_allreduce_emulated")
     return out, workspace
 
 
@@ -198,13 +227,15 @@ def fc_sum_uncompressed(x: torch.Tensor, out=None, stream=None):
     return out
 
 
-def workspace_views(workspace: torch.Tensor, R: int, T: int, H: int, bits: int, group: int) -> dict:
+def workspace_views(workspace: torch.Tensor, R: int, T: int, H: int, bits: int, group: int,
+                    bits2: int | None = None) -> dict:
     """Views of the payloads inside an fc_allreduce_emulated workspace."""
-    lay = fc_workspace_layout(R, T, H, bits, group)
+    bits2 = bits if bits2 is None else bits2
+    lay = fc_workspace_layout(R, T, H, bits, group, bits2)
     g2 = fc_stage2_group(R, H, group)
     names = ("codes1", "s1", "z1", "codes2", "s2", "z2")
     shapes = ((R, T, H * bits // 8), (R, T, H // group), (R, T, H // group),
-              (T, H * bits // 8), (T, H // g2), (T, H // g2))
+              (T, H * bits2 // 8), (T, H // g2), (T, H // g2))
     out = {}
     for name, (off, size), shape in zip(names, lay, shapes):
         raw = workspace[off:off + size]

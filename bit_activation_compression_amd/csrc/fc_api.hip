@@ -50,14 +50,14 @@ struct Layout {
     size_t total;
 };
 
-Layout layout(int R, int T, int H, int bits, int group, int g2) {
+Layout layout(int R, int T, int H, int bits1, int bits2, int group, int g2) {
     const size_t n1 = (size_t)R * (size_t)T * (size_t)H;
     const size_t n2 = (size_t)T * (size_t)H;
     Layout L;
-    L.size[0] = n1 * (size_t)bits / 8;
+    L.size[0] = n1 * (size_t)bits1 / 8;
     L.size[1] = n1 / (size_t)group * 2;
     L.size[2] = L.size[1];
-    L.size[3] = n2 * (size_t)bits / 8;
+    L.size[3] = n2 * (size_t)bits2 / 8;
     L.size[4] = n2 / (size_t)g2 * 2;
     L.size[5] = L.size[4];
     size_t o = 0;
@@ -67,6 +67,14 @@ Layout layout(int R, int T, int H, int bits, int group, int g2) {
     }
     L.total = o;
     return L;
+}
+
+// Shape and both code widths; on success sets g2.
+fc_status check_shape2(int R, int T, int H, int bits1, int bits2, int group, int *g2) {
+    fc_status st = check_shape(R, T, H, bits1, group, g2);
+    if (st != FC_OK) return st;
+    if (bits2 != 4 && bits2 != 8) return FC_ERR_BITS;
+    return FC_OK;
 }
 
 }  // namespace
@@ -86,17 +94,25 @@ fc_status fc_quantize_groups(const void *x, fc_dtype dt, int R, int T, int H, in
                                         codes1, s1, z1, static_cast<hipStream_t>(stream)));
 }
 
-fc_status fc_dequant_sum_requant(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1,
-                                 int R, int T, int H, int bits, int group,
-                                 uint8_t *codes2, uint16_t *s2, uint16_t *z2, void *stream) {
+fc_status fc_dequant_sum_requant_mixed(const uint8_t *codes1, const uint16_t *s1,
+                                       const uint16_t *z1, int R, int T, int H, int bits1,
+                                       int bits2, int group, uint8_t *codes2, uint16_t *s2,
+                                       uint16_t *z2, void *stream) {
     int g2 = 0;
-    fc_status st = check_shape(R, T, H, bits, group, &g2);
+    fc_status st = check_shape2(R, T, H, bits1, bits2, group, &g2);
     if (st != FC_OK) return st;
     const uint64_t n = (uint64_t)T * (uint64_t)H;
     st = check_ptrs(n, {codes1, s1, z1, codes2, s2, z2});
     if (st != FC_OK || n == 0) return st;
-    return from_hip(fc::launch_dequant_sum_requant(codes1, s1, z1, R, n, bits, group, g2, codes2, s2,
-                                                   z2, static_cast<hipStream_t>(stream)));
+    return from_hip(fc::launch_dequant_sum_requant(codes1, s1, z1, R, n, bits1, bits2, group, g2,
+                                                   codes2, s2, z2, static_cast<hipStream_t>(stream)));
+}
+
+fc_status fc_dequant_sum_requant(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1,
+                                 int R, int T, int H, int bits, int group,
+                                 uint8_t *codes2, uint16_t *s2, uint16_t *z2, void *stream) {
+    return fc_dequant_sum_requant_mixed(codes1, s1, z1, R, T, H, bits, bits, group, codes2, s2, z2,
+                                        stream);
 }
 
 fc_status fc_dequantize(const uint8_t *codes2, const uint16_t *s2, const uint16_t *z2,
@@ -112,16 +128,17 @@ fc_status fc_dequantize(const uint8_t *codes2, const uint16_t *s2, const uint16_
                                           static_cast<hipStream_t>(stream)));
 }
 
-fc_status fc_allreduce_emulated(const void *x, fc_dtype dt, int R, int T, int H, int bits, int group,
-                                void *out, void *workspace, size_t workspace_bytes, void *stream) {
+fc_status fc_allreduce_emulated_mixed(const void *x, fc_dtype dt, int R, int T, int H, int bits1,
+                                      int bits2, int group, void *out, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
     int g2 = 0;
-    fc_status st = check_shape(R, T, H, bits, group, &g2);
+    fc_status st = check_shape2(R, T, H, bits1, bits2, group, &g2);
     if (st != FC_OK) return st;
     if (dt != FC_F16 && dt != FC_BF16) return FC_ERR_DTYPE;
     const uint64_t n = (uint64_t)T * (uint64_t)H;
     st = check_ptrs(n, {x, out, workspace});
     if (st != FC_OK) return st;
-    const Layout L = layout(R, T, H, bits, group, g2);
+    const Layout L = layout(R, T, H, bits1, bits2, group, g2);
     if (n != 0 && workspace_bytes < L.total) return FC_ERR_WORKSPACE;
     if (n == 0) return FC_OK;
     uint8_t *ws = static_cast<uint8_t *>(workspace);
@@ -132,13 +149,20 @@ fc_status fc_allreduce_emulated(const void *x, fc_dtype dt, int R, int T, int H,
     uint16_t *s2 = reinterpret_cast<uint16_t *>(ws + L.off[4]);
     uint16_t *z2 = reinterpret_cast<uint16_t *>(ws + L.off[5]);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    st = from_hip(fc::launch_quantize(static_cast<const uint16_t *>(x), (int)dt, n * (uint64_t)R, bits,
+    st = from_hip(fc::launch_quantize(static_cast<const uint16_t *>(x), (int)dt, n * (uint64_t)R, bits1,
                                       group, codes1, s1, z1, s));
     if (st != FC_OK) return st;
-    st = from_hip(fc::launch_dequant_sum_requant(codes1, s1, z1, R, n, bits, group, g2, codes2, s2, z2, s));
+    st = from_hip(fc::launch_dequant_sum_requant(codes1, s1, z1, R, n, bits1, bits2, group, g2, codes2,
+                                                 s2, z2, s));
     if (st != FC_OK) return st;
-    return from_hip(fc::launch_dequantize(codes2, s2, z2, n, bits, g2, (int)dt,
+    return from_hip(fc::launch_dequantize(codes2, s2, z2, n, bits2, g2, (int)dt,
                                           static_cast<uint16_t *>(out), s));
+}
+
+fc_status fc_allreduce_emulated(const void *x, fc_dtype dt, int R, int T, int H, int bits, int group,
+                                void *out, void *workspace, size_t workspace_bytes, void *stream) {
+    return fc_allreduce_emulated_mixed(x, dt, R, T, H, bits, bits, group, out, workspace,
+                                       workspace_bytes, stream);
 }
 
 fc_status fc_sum_uncompressed(const void *x, fc_dtype dt, int R, int T, int H, void *out,
@@ -152,24 +176,33 @@ fc_status fc_sum_uncompressed(const void *x, fc_dtype dt, int R, int T, int H, v
                                    static_cast<uint16_t *>(out), static_cast<hipStream_t>(stream)));
 }
 
-size_t fc_workspace_bytes(int R, int T, int H, int bits, int group) {
+size_t fc_workspace_bytes_mixed(int R, int T, int H, int bits1, int bits2, int group) {
     int g2 = 0;
-    if (check_shape(R, T, H, bits, group, &g2) != FC_OK) return 0;
-    return layout(R, T, H, bits, group, g2).total;
+    if (check_shape2(R, T, H, bits1, bits2, group, &g2) != FC_OK) return 0;
+    return layout(R, T, H, bits1, bits2, group, g2).total;
 }
 
-fc_status fc_workspace_layout(int R, int T, int H, int bits, int group, size_t offsets[6],
-                              size_t sizes[6]) {
+size_t fc_workspace_bytes(int R, int T, int H, int bits, int group) {
+    return fc_workspace_bytes_mixed(R, T, H, bits, bits, group);
+}
+
+fc_status fc_workspace_layout_mixed(int R, int T, int H, int bits1, int bits2, int group,
+                                    size_t offsets[6], size_t sizes[6]) {
     int g2 = 0;
-    fc_status st = check_shape(R, T, H, bits, group, &g2);
+    fc_status st = check_shape2(R, T, H, bits1, bits2, group, &g2);
     if (st != FC_OK) return st;
     if (offsets == nullptr || sizes == nullptr) return FC_ERR_NULL;
-    const Layout L = layout(R, T, H, bits, group, g2);
+    const Layout L = layout(R, T, H, bits1, bits2, group, g2);
     for (int i = 0; i < 6; ++i) {
         offsets[i] = L.off[i];
         sizes[i] = L.size[i];
     }
     return FC_OK;
+}
+
+fc_status fc_workspace_layout(int R, int T, int H, int bits, int group, size_t offsets[6],
+                              size_t sizes[6]) {
+    return fc_workspace_layout_mixed(R, T, H, bits, bits, group, offsets, sizes);
 }
 
 int fc_stage2_group(int R, int H, int group) {

@@ -9,12 +9,14 @@
 // to flat groups of g2: position p reads code p of every operand r (operand
 // stride n), dequantizes each with its own stage-1 scale and zero, sums them
 // in binary32 in ascending r starting from operand 0, and the sums are
-// requantized like stage 1.
+// requantized like stage 1. The incoming codes are BITS1 wide, the outgoing
+// ones BITS2 (the same unless the caller asks for different widths).
 //
-// Per output element it reads R*bits/8 code bytes (plus 4 bytes per stage-1
-// group and operand) and writes bits/8 code bytes (plus 4 per stage-2 group).
-// The fp32 work per element grows with R (decode, fma, add per operand), so
-// for R = 4 the kernel is bound by vector ALU issue rather than by HBM.
+// Per output element it reads R*bits1/8 code bytes (plus 4 bytes per stage-1
+// group and operand) and writes bits2/8 code bytes (plus 4 per stage-2
+// group). The fp32 work per element grows with R (decode, fma, add per
+// operand), so for R = 4 the kernel is bound by vector ALU issue rather than
+// by HBM.
 #include "fc_device.h"
 #include "fc_launch.h"
 
@@ -25,16 +27,14 @@ namespace {
 // are issued before the first use); RT == 0: any R, one operand at a time.
 constexpr int base_slots(int RT) { return RT >= 8 ? 2 : 4; }
 
-template <int BITS, int G2, int RT>
+template <int BITS1, int BITS2, int G2, int RT>
 __global__ __launch_bounds__(kBlockThreads) void dsr_kernel(
     const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ s1,
     const uint16_t *__restrict__ z1, int R_arg, uint64_t n, int g1_shift,
     uint8_t *__restrict__ codes2, uint16_t *__restrict__ s2, uint16_t *__restrict__ z2) {
     constexpr int U = tile_slots(G2, base_slots(RT));
-    constexpr int S = G2 > kSlotElems ? G2 / kSlotElems : 1;
-    constexpr int L = G2 >= kSlotElems ? kWave : G2 / kLaneElems;
-    constexpr int W = BITS == 4 ? 1 : 2;
-    static_assert(U % S == 0 && (U * kSlotElems) % G2 == 0, "a tile holds whole groups");
+    constexpr int W = BITS1 == 4 ? 1 : 2;
+    static_assert((U * kSlotElems) % G2 == 0, "tiles start on a group boundary");
     const int R = RT > 0 ? RT : R_arg;
 
     const int lane = lane_id();
@@ -52,25 +52,23 @@ __global__ __launch_bounds__(kBlockThreads) void dsr_kernel(
     // element instead, so every load is unconditional and all of a tile's
     // loads are in flight together; only their stores are skipped.
     const uint32_t mis = (uint32_t)tile & ((1u << g1_shift) - 1u);
-    uint32_t rel[U], lrel[U], mrel[U];
-    bool ok[U];
+    uint32_t lrel[U], mrel[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        rel[u] = u * kSlotElems + lane * kLaneElems;
-        ok[u] = rel[u] < avail;
-        lrel[u] = ok[u] ? rel[u] : 0u;
+        const uint32_t rel = u * kSlotElems + lane * kLaneElems;
+        lrel[u] = rel < avail ? rel : 0u;
         mrel[u] = (mis + lrel[u]) >> g1_shift;
     }
 
     float y[U][kLaneElems];
     auto load_operand = [&](int r, uint32_t (&w)[U][W], uint16_t (&sv)[U], uint16_t (&zv)[U]) {
         const uint64_t e0 = (uint64_t)r * n + tile;
-        const uint8_t *cb = codes1 + e0 * BITS / 8;
+        const uint8_t *cb = codes1 + e0 * BITS1 / 8;
         const uint16_t *sb = s1 + (e0 >> g1_shift);
         const uint16_t *zb = z1 + (e0 >> g1_shift);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            load_codes<BITS, false>(cb, lrel[u], w[u]);
+            load_codes<BITS1, false>(cb, lrel[u], w[u]);
             sv[u] = sb[mrel[u]];
             zv[u] = zb[mrel[u]];
         }
@@ -82,7 +80,7 @@ __global__ __launch_bounds__(kBlockThreads) void dsr_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float q[kLaneElems];
-            decode8<BITS>(w[u], q);
+            decode8<BITS1>(w[u], q);
             const float s = half_bits_to_float(sv[u]);
             const float z = half_bits_to_float(zv[u]);
 #pragma unroll
@@ -112,39 +110,14 @@ __global__ __launch_bounds__(kBlockThreads) void dsr_kernel(
     }
 
     // requantize the sums in groups of G2 (tiles start on a group boundary)
-    uint8_t *cb = codes2 + tile * BITS / 8;
-    uint16_t *sb = s2 + tile / G2;
-    uint16_t *zb = z2 + tile / G2;
     float mn[U], mx[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) minmax8(y[u], mn[u], mx[u]);
-#pragma unroll
-    for (int g = 0; g < U / S; ++g) {
-        float a = mn[g * S], b = mx[g * S];
-#pragma unroll
-        for (int k = 1; k < S; ++k) {
-            a = __builtin_fminf(a, mn[g * S + k]);
-            b = __builtin_fmaxf(b, mx[g * S + k]);
-        }
-        lanes_minmax<L>(a, b);
-        const GroupParams p = group_params<BITS>(a, b);
-#pragma unroll
-        for (int k = 0; k < S; ++k) {
-            const int u = g * S + k;
-            if (!ok[u]) continue;
-            uint32_t w[W];
-            encode8<BITS>(y[u], p, w);
-            store_codes<BITS, false>(cb, rel[u], w);
-            const bool leader = (S > 1) ? (k == 0 && lane == 0) : (lane % L == 0);
-            if (leader) {
-                sb[rel[u] / G2] = p.s16;
-                zb[rel[u] / G2] = p.z16;
-            }
-        }
-    }
+    quantize_tile<BITS2, G2, U, false>(y, mn, mx, lane, avail, codes2 + tile * BITS2 / 8,
+                                       s2 + tile / G2, z2 + tile / G2);
 }
 
-template <int BITS, int G2, int RT>
+template <int BITS1, int BITS2, int G2, int RT>
 hipError_t launch_one(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1, int R,
                       uint64_t n, int g1_shift, uint8_t *codes2, uint16_t *s2, uint16_t *z2,
                       hipStream_t stream) {
@@ -152,33 +125,36 @@ hipError_t launch_one(const uint8_t *codes1, const uint16_t *s1, const uint16_t 
         (uint64_t)kWavesPerBlock * tile_slots(G2, base_slots(RT)) * kSlotElems;
     const uint64_t blocks = (n + per_block - 1) / per_block;
     if (blocks > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((dsr_kernel<BITS, G2, RT>), dim3((unsigned)blocks), dim3(kBlockThreads), 0,
-                       stream, codes1, s1, z1, R, n, g1_shift, codes2, s2, z2);
+    hipLaunchKernelGGL((dsr_kernel<BITS1, BITS2, G2, RT>), dim3((unsigned)blocks), dim3(kBlockThreads),
+                       0, stream, codes1, s1, z1, R, n, g1_shift, codes2, s2, z2);
     return hipGetLastError();
 }
 
-template <int BITS, int G2>
+template <int BITS1, int BITS2, int G2>
 hipError_t dispatch_r(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1, int R,
                       uint64_t n, int g1_shift, uint8_t *codes2, uint16_t *s2, uint16_t *z2,
                       hipStream_t stream) {
     // The compile-time operand count keeps R x U code words in flight; it is
     // used only where a tile is the base size, so registers stay bounded.
+#define FC_LAUNCH(RT) \
+    launch_one<BITS1, BITS2, G2, RT>(codes1, s1, z1, R, n, g1_shift, codes2, s2, z2, stream)
     if constexpr (G2 <= kSlotElems * base_slots(8)) {
-        if (R == 8) return launch_one<BITS, G2, 8>(codes1, s1, z1, R, n, g1_shift, codes2, s2, z2, stream);
+        if (R == 8) return FC_LAUNCH(8);
     }
     if constexpr (G2 <= kSlotElems * base_slots(4)) {
-        if (R == 4) return launch_one<BITS, G2, 4>(codes1, s1, z1, R, n, g1_shift, codes2, s2, z2, stream);
-        if (R == 2) return launch_one<BITS, G2, 2>(codes1, s1, z1, R, n, g1_shift, codes2, s2, z2, stream);
+        if (R == 4) return FC_LAUNCH(4);
+        if (R == 2) return FC_LAUNCH(2);
     }
-    return launch_one<BITS, G2, 0>(codes1, s1, z1, R, n, g1_shift, codes2, s2, z2, stream);
+    return FC_LAUNCH(0);
+#undef FC_LAUNCH
 }
 
-template <int BITS>
+template <int BITS1, int BITS2>
 hipError_t dispatch_group(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1, int R,
                           uint64_t n, int g1_shift, int group2, uint8_t *codes2, uint16_t *s2,
                           uint16_t *z2, hipStream_t stream) {
 #define FC_CASE(G) \
-    case G: return dispatch_r<BITS, G>(codes1, s1, z1, R, n, g1_shift, codes2, s2, z2, stream);
+    case G: return dispatch_r<BITS1, BITS2, G>(codes1, s1, z1, R, n, g1_shift, codes2, s2, z2, stream);
     switch (group2) {
         FC_CASE(8) FC_CASE(16) FC_CASE(32) FC_CASE(64) FC_CASE(128) FC_CASE(256) FC_CASE(512)
         FC_CASE(1024) FC_CASE(2048) FC_CASE(4096) FC_CASE(8192)
@@ -190,12 +166,15 @@ hipError_t dispatch_group(const uint8_t *codes1, const uint16_t *s1, const uint1
 }  // namespace
 
 hipError_t launch_dequant_sum_requant(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1,
-                                      int R, uint64_t n, int bits, int group1, int group2,
-                                      uint8_t *codes2, uint16_t *s2, uint16_t *z2,
+                                      int R, uint64_t n, int bits1, int bits2, int group1,
+                                      int group2, uint8_t *codes2, uint16_t *s2, uint16_t *z2,
                                       hipStream_t stream) {
-    const int g1_shift = ilog2(group1);
-    return bits == 4 ? dispatch_group<4>(codes1, s1, z1, R, n, g1_shift, group2, codes2, s2, z2, stream)
-                     : dispatch_group<8>(codes1, s1, z1, R, n, g1_shift, group2, codes2, s2, z2, stream);
+    const int sh = ilog2(group1);
+    if (bits1 == 4)
+        return bits2 == 4 ? dispatch_group<4, 4>(codes1, s1, z1, R, n, sh, group2, codes2, s2, z2, stream)
+                          : dispatch_group<4, 8>(codes1, s1, z1, R, n, sh, group2, codes2, s2, z2, stream);
+    return bits2 == 4 ? dispatch_group<8, 4>(codes1, s1, z1, R, n, sh, group2, codes2, s2, z2, stream)
+                      : dispatch_group<8, 8>(codes1, s1, z1, R, n, sh, group2, codes2, s2, z2, stream);
 }
 
 }  // namespace fc

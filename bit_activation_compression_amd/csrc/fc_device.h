@@ -277,6 +277,47 @@ __device__ __forceinline__ void decode8(const uint32_t (&w)[BITS == 4 ? 1 : 2], 
     }
 }
 
+// Quantize a tile of U slots: v holds the lane's 8 values per slot, mn/mx
+// their in-lane minima and maxima. Each group's min/max is reduced over its
+// S slots and L lanes, its scale/zero/reciprocal computed, and the codes
+// written to cb (NT: non-temporal) and the fp16 scale and zero of every group
+// to sb and zb (bases of the tile's first group). Slots at or past `avail`
+// elements are not stored.
+template <int BITS, int G, int U, bool NT>
+__device__ __forceinline__ void quantize_tile(const float (&v)[U][kLaneElems], const float (&mn)[U],
+                                              const float (&mx)[U], int lane, uint32_t avail,
+                                              uint8_t *cb, uint16_t *sb, uint16_t *zb) {
+    constexpr int S = G > kSlotElems ? G / kSlotElems : 1;        // slots per group
+    constexpr int L = G >= kSlotElems ? kWave : G / kLaneElems;   // lanes per group in a slot
+    constexpr int W = BITS == 4 ? 1 : 2;
+    static_assert(U % S == 0 && (U * kSlotElems) % G == 0, "a tile holds whole groups");
+#pragma unroll
+    for (int g = 0; g < U / S; ++g) {
+        float a = mn[g * S], b = mx[g * S];
+#pragma unroll
+        for (int k = 1; k < S; ++k) {
+            a = __builtin_fminf(a, mn[g * S + k]);
+            b = __builtin_fmaxf(b, mx[g * S + k]);
+        }
+        lanes_minmax<L>(a, b);
+        const GroupParams p = group_params<BITS>(a, b);
+#pragma unroll
+        for (int k = 0; k < S; ++k) {
+            const int u = g * S + k;
+            const uint32_t rel = u * kSlotElems + lane * kLaneElems;
+            if (rel >= avail) continue;
+            uint32_t w[W];
+            encode8<BITS>(v[u], p, w);
+            store_codes<BITS, NT>(cb, rel, w);
+            const bool leader = (S > 1) ? (k == 0 && lane == 0) : (lane % L == 0);
+            if (leader) {
+                sb[rel / G] = p.s16;
+                zb[rel / G] = p.z16;
+            }
+        }
+    }
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
     return (float)__builtin_bit_cast(_Float16, b);
 }

@@ -13,10 +13,11 @@ hipError_t launch_quantize(const uint16_t *x, int dtype, uint64_t n, int bits, i
                            uint8_t *codes, uint16_t *s, uint16_t *z, hipStream_t stream);
 
 // Reduce-scatter reduction + requantization over n = T*H positions of R
-// operands laid out [R][n]: stage-1 groups of `group1`, stage-2 groups of `group2`.
+// operands laid out [R][n]: stage-1 codes of bits1 in groups of `group1`,
+// stage-2 codes of bits2 in groups of `group2`.
 hipError_t launch_dequant_sum_requant(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1,
-                                      int R, uint64_t n, int bits, int group1, int group2,
-                                      uint8_t *codes2, uint16_t *s2, uint16_t *z2,
+                                      int R, uint64_t n, int bits1, int bits2, int group1,
+                                      int group2, uint8_t *codes2, uint16_t *s2, uint16_t *z2,
                                       hipStream_t stream);
 
 // Final dequantization of n codes in groups of `group2` into 16-bit outputs.

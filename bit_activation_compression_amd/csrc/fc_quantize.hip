@@ -25,10 +25,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_kernel(
     const uint16_t *__restrict__ x, uint64_t n, uint8_t *__restrict__ codes,
     uint16_t *__restrict__ s_out, uint16_t *__restrict__ z_out) {
     constexpr int U = tile_slots(G, kTileSlots);                   // slots per wave tile
-    constexpr int S = G > kSlotElems ? G / kSlotElems : 1;        // slots per group
-    constexpr int L = G >= kSlotElems ? kWave : G / kLaneElems;   // lanes per group in a slot
-    constexpr int W = BITS == 4 ? 1 : 2;
-    static_assert(U % S == 0 && (U * kSlotElems) % G == 0, "a tile holds whole groups");
+    static_assert((U * kSlotElems) % G == 0, "tiles start on a group boundary");
 
     const int lane = lane_id();
     const uint64_t wave = wave_index();
@@ -57,32 +54,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_kernel(
     float mn[U], mx[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) minmax8(v[u], mn[u], mx[u]);
-
-#pragma unroll
-    for (int g = 0; g < U / S; ++g) {
-        float a = mn[g * S], b = mx[g * S];
-#pragma unroll
-        for (int k = 1; k < S; ++k) {
-            a = __builtin_fminf(a, mn[g * S + k]);
-            b = __builtin_fmaxf(b, mx[g * S + k]);
-        }
-        lanes_minmax<L>(a, b);
-        const GroupParams p = group_params<BITS>(a, b);
-#pragma unroll
-        for (int k = 0; k < S; ++k) {
-            const int u = g * S + k;
-            const uint32_t rel = u * kSlotElems + lane * kLaneElems;
-            if (rel >= avail) continue;
-            uint32_t w[W];
-            encode8<BITS>(v[u], p, w);
-            store_codes<BITS, true>(cb, rel, w);
-            const bool leader = (S > 1) ? (k == 0 && lane == 0) : (lane % L == 0);
-            if (leader) {
-                sb[rel / G] = p.s16;
-                zb[rel / G] = p.z16;
-            }
-        }
-    }
+    quantize_tile<BITS, G, U, true>(v, mn, mx, lane, avail, cb, sb, zb);
 }
 
 template <int DT, int BITS, int G>

@@ -111,6 +111,31 @@ fc_status fc_allreduce_emulated(const void *x, fc_dtype dt, int R, int T, int H,
                                 void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Different code widths before the two steps. The page quantizes before the
+ * Reduce-Scatter and before the All-Gather and contrasts the two steps'
+ * errors (Figure 5, right) without fixing the widths; these variants take
+ * bits1 for the stage-1 payload (codes1) and bits2 for the stage-2 payload
+ * (codes2), each 4 or 8 (FC_ERR_BITS otherwise). With bits1 == bits2 they are
+ * fc_dequant_sum_requant and fc_allreduce_emulated.
+ *   codes1 [R][T][H*bits1/8], codes2 [T][H*bits2/8]; the final dequantize of
+ *   codes2 uses bits2.
+ */
+fc_status fc_dequant_sum_requant_mixed(const uint8_t *codes1, const uint16_t *s1,
+                                       const uint16_t *z1, int R, int T, int H, int bits1,
+                                       int bits2, int group, uint8_t *codes2, uint16_t *s2,
+                                       uint16_t *z2, void *stream);
+
+fc_status fc_allreduce_emulated_mixed(const void *x, fc_dtype dt, int R, int T, int H, int bits1,
+                                      int bits2, int group, void *out, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/* Workspace size and layout for the mixed-width pipeline (same slice order). */
+size_t fc_workspace_bytes_mixed(int R, int T, int H, int bits1, int bits2, int group);
+
+fc_status fc_workspace_layout_mixed(int R, int T, int H, int bits1, int bits2, int group,
+                                    size_t offsets[6], size_t sizes[6]);
+
+/*
  * The uncompressed all-reduce result the page compares against (Figure 1: an
  * NCCL Ring All-Reduce of FP16 activations), computed on one GPU as the
  * reference point for the codec's speed and error:

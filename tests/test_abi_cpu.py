@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     L = fc.lib()
     names = _declared_functions()
-    assert len(names) == 9
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), n
     assert sorted(names) == sorted(fc.EXPORTED_SYMBOLS)
@@ -62,6 +62,10 @@ def test_workspace_layout_matches_payload_sizes():
     total = fc.fc_workspace_bytes(R, T, H, bits, g)
     assert total >= offs[5] + sizes[5] and total - (offs[5] + sizes[5]) < 256
     assert fc.fc_workspace_bytes(4, 8192, 8192, 5, 128) == 0
+    lay48 = fc.fc_workspace_layout(R, T, H, 4, g, bits2=8)
+    assert [s for _, s in lay48][0] == R * T * H // 2 and [s for _, s in lay48][3] == T * H
+    lay84 = fc.fc_workspace_layout(R, T, H, 8, g, bits2=4)
+    assert [s for _, s in lay84][0] == R * T * H and [s for _, s in lay84][3] == T * H // 2
 
 
 def _q(*args):
@@ -109,3 +113,9 @@ def test_other_entry_points_validate():
     assert L.fc_sum_uncompressed(FAKE, 3, 2, 8, 256, FAKE, None) == 7
     assert L.fc_sum_uncompressed(MISALIGNED, 0, 2, 8, 256, FAKE, None) == 4
     assert L.fc_sum_uncompressed(None, 0, 2, 0, 256, None, None) == 0
+    # mixed widths
+    assert L.fc_dequant_sum_requant_mixed(FAKE, FAKE, FAKE, 2, 8, 256, 4, 6, 128, FAKE, FAKE, FAKE, None) == 3
+    assert L.fc_dequant_sum_requant_mixed(FAKE, FAKE, FAKE, 2, 8, 256, 5, 8, 128, FAKE, FAKE, FAKE, None) == 3
+    need = fc.fc_workspace_bytes(2, 8, 256, 4, 128, bits2=8)
+    assert L.fc_allreduce_emulated_mixed(FAKE, 0, 2, 8, 256, 4, 8, 128, FAKE, FAKE, need - 1, None) == 5
+    assert L.fc_allreduce_emulated_mixed(None, 0, 2, 0, 256, 4, 8, 128, None, None, 0, None) == 0

@@ -57,24 +57,25 @@ def _np(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
-def _run_fused(x: np.ndarray, w: synth.Workload) -> dict:
+def _run_fused(x: np.ndarray, w: synth.Workload, bits2: int | None = None) -> dict:
     R, T, H = x.shape
     xd = _to_dev(x, w.dtype)
-    out, ws = fc.fc_allreduce_emulated(xd, w.bits, w.group)
-    views = fc.workspace_views(ws, R, T, H, w.bits, w.group)
+    out, ws = fc.fc_allreduce_emulated(xd, w.bits, w.group, bits2=bits2)
+    views = fc.workspace_views(ws, R, T, H, w.bits, w.group, bits2=bits2)
     torch.cuda.synchronize()
     got = {k: _np(v) for k, v in views.items()}
     got["out"] = _np(out)
     return got
 
 
-def _run_steps(x: np.ndarray, w: synth.Workload) -> dict:
+def _run_steps(x: np.ndarray, w: synth.Workload, bits2: int | None = None) -> dict:
     R, T, H = x.shape
+    b2 = w.bits if bits2 is None else bits2
     xd = _to_dev(x, w.dtype)
     c1, s1, z1 = fc.fc_quantize_groups(xd, w.bits, w.group)
-    c2, s2, z2 = fc.fc_dequant_sum_requant(c1, s1, z1, R, T, H, w.bits, w.group)
+    c2, s2, z2 = fc.fc_dequant_sum_requant(c1, s1, z1, R, T, H, w.bits, w.group, bits2=b2)
     g2 = fc.fc_stage2_group(R, H, w.group)
-    out = fc.fc_dequantize(c2, s2, z2, T, H, w.bits, g2, TDT[w.dtype])
+    out = fc.fc_dequantize(c2, s2, z2, T, H, b2, g2, TDT[w.dtype])
     torch.cuda.synchronize()
     return {k: _np(v) for k, v in zip(PAYLOAD + ("out",), (c1, s1, z1, c2, s2, z2, out))}
 
@@ -234,3 +235,32 @@ def test_repeat_runs_and_entry_points_agree():
     c = _run_steps(x, w)
     for k in PAYLOAD + ("out",):
         assert np.array_equal(a[k], b[k]) and np.array_equal(a[k], c[k]), k
+
+
+# ---------------------------------------------------------------------------
+# different code widths before the reduce-scatter and the all-gather
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits,bits2", [(4, 8), (8, 4)])
+@pytest.mark.parametrize("name", ["llama3_70b_prefill", "llama3_8b_prefill", "decode", "sweep_int4_g4096"])
+def test_mixed_widths(name, bits, bits2):
+    w = synth.workload(name).with_(bits=bits)
+    if w.T > 1024:
+        w = w.with_(T=1024)
+    x = synth.operands(w, 2)
+    ref = oracle.allreduce(x, w.dtype, bits, w.group, want_f32=False, bits2=bits2)
+    _say(f"mixed widths {name} T={w.T} bits {bits}->{bits2}")
+    _check(_run_fused(x, w, bits2), ref, w, x)
+    _check(_run_steps(x, w, bits2), ref, w, x)
+
+
+@pytest.mark.parametrize("R,T,H,group", [(3, 7, 384, 128), (8, 9, 8192, 8192), (2, 33, 1024, 8),
+                                         (5, 3, 640, 128), (6, 11, 3072, 512)])
+def test_mixed_widths_ragged(R, T, H, group):
+    for bits, bits2 in ((4, 8), (8, 4)):
+        w = synth.workload("tiny").with_(R=R, T=T, H=H, bits=bits, group=group, dtype=synth.BF16,
+                                         outlier_frac=0.01, outlier_scale=20.0)
+        x = synth.operands(w, 5)
+        ref = oracle.allreduce(x, w.dtype, bits, group, want_f32=False, bits2=bits2)
+        _say(f"mixed widths ragged R={R} T={T} H={H} g={group} bits {bits}->{bits2}")
+        _check(_run_fused(x, w, bits2), ref, w, x)
