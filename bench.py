@@ -95,6 +95,108 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+def quality_report(seed: int) -> int:
+    """Error of the codec at each stage, as in Figure 4 (activation quantization with blocks
+    from the hidden length down to 128) and Figure 5 right (quantization before the
+    Reduce-Scatter vs before the All-Gather), on the synthetic operands; plus throughput.
+    The codec runs in the library's kernels; the error statistics (and the binary32
+    dequantized values they need) are computed with torch on the GPU from the payloads
+    the library wrote.
+      stage1_mse: mean over r, t, h of (dequantized payload 1 - x)^2
+      stage2_mse: mean of (dequantized payload 2 - sum_r dequantized payload 1)^2
+      total_mse : mean of (output - sum_r x)^2
+    Prints one JSON line with a record per configuration."""
+    import numpy as np
+    import torch
+
+    import bit_activation_compression_amd as fc
+    import synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    names = [f"sweep_int{b}_g{g}" for b in synth.SWEEP_BITS for g in synth.SWEEP_GROUPS]
+    names += ["tiny", "llama3_8b_prefill", "llama3_70b_prefill", "decode"]
+    widths = {n: [(synth.workload(n).bits, synth.workload(n).bits)] for n in names}
+    widths["llama3_70b_prefill"] += [(4, 8), (8, 4), (8, 8)]
+    widths["llama3_8b_prefill"] += [(4, 8), (8, 4), (8, 8)]
+    records = []
+    for name in names:
+        w = synth.workload(name)
+        R, T, H, g = w.R, w.T, w.H, w.group
+        tdt = torch.bfloat16 if w.dtype == synth.BF16 else torch.float16
+        x_host = synth.operands(w, seed)
+        xd = torch.from_numpy(x_host.view(np.int16)).to(dev).view(tdt)
+        xf = xd.float()
+        exact = xf.sum(dim=0)
+        for bits, bits2 in widths[name]:
+            g2 = fc.fc_stage2_group(R, H, g)
+            out, ws = fc.fc_allreduce_emulated(xd, bits, g, bits2=bits2)
+            v = fc.workspace_views(ws, R, T, H, bits, g, bits2=bits2)
+            # the dequantized stage values in binary32, as the receiver sums them
+            s1 = v["s1"].view(torch.float16).float().repeat_interleave(g, dim=2)
+            z1 = v["z1"].view(torch.float16).float().repeat_interleave(g, dim=2)
+            c1 = v["codes1"]
+            q1 = torch.stack([c1 & 15, c1 >> 4], dim=-1).reshape(R, T, H) if bits == 4 else c1
+            xh32 = q1.float() * s1 + z1
+            y = xh32[0].clone()
+            for r in range(1, R):
+                y = y + xh32[r]
+            s2 = v["s2"].view(torch.float16).float().repeat_interleave(g2, dim=1)
+            z2 = v["z2"].view(torch.float16).float().repeat_interleave(g2, dim=1)
+            c2 = v["codes2"]
+            q2 = torch.stack([c2 & 15, c2 >> 4], dim=-1).reshape(T, H) if bits2 == 4 else c2
+            yh = q2.float() * s2 + z2
+            rec = {"workload": name, "bits_rs": bits, "bits_ag": bits2, "group": g, "group2": g2,
+                   "stage1_mse": float(((xh32 - xf) ** 2).mean()),
+                   "stage2_mse": float(((yh - y) ** 2).mean()),
+                   "total_mse": float(((out.float() - exact) ** 2).mean()),
+                   "exact_sum_power": float((exact ** 2).mean())}
+            del s1, z1, q1, xh32, y, s2, z2, q2, yh
+            # throughput of the whole path on this configuration
+            for _ in range(5):
+                fc.fc_allreduce_emulated(xd, bits, g, out, ws, stream=stream, bits2=bits2)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for _ in range(20):
+                fc.fc_allreduce_emulated(xd, bits, g, out, ws, stream=stream, bits2=bits2)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ms = ev[0].elapsed_time(ev[1]) / 20
+            n1, n2 = R * T * H, T * H
+            p1 = n1 * bits // 8 + n1 // g * 4
+            p2 = n2 * bits2 // 8 + n2 // g2 * 4
+            total = n1 * 2 + 2 * p1 + 2 * p2 + n2 * 2
+            rec.update({"us_per_call": round(ms * 1e3, 2), "gbps": round(total / (ms * 1e-3) / 1e9, 1)})
+            if T * H <= 1 << 20:
+                # launch-bound shapes: the same call captured once in a HIP graph and replayed
+                graph = torch.cuda.CUDAGraph()
+                cap = torch.cuda.Stream(dev)
+                cap.wait_stream(stream)
+                with torch.cuda.stream(cap):
+                    fc.fc_allreduce_emulated(xd, bits, g, out, ws, stream=cap, bits2=bits2)
+                    with torch.cuda.graph(graph, stream=cap):
+                        fc.fc_allreduce_emulated(xd, bits, g, out, ws, stream=cap, bits2=bits2)
+                stream.wait_stream(cap)
+                torch.cuda.synchronize()
+                for _ in range(5):
+                    graph.replay()
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                ev[0].record(stream)
+                for _ in range(50):
+                    graph.replay()
+                ev[1].record(stream)
+                torch.cuda.synchronize()
+                rec["us_per_call_graph"] = round(ev[0].elapsed_time(ev[1]) / 50 * 1e3, 2)
+                del graph
+            records.append(rec)
+            print(f"[quality] {name} int{bits}->int{bits2}: stage1 {rec['stage1_mse']:.4g} "
+                  f"stage2 {rec['stage2_mse']:.4g} total {rec['total_mse']:.4g} "
+                  f"{rec['us_per_call']} us {rec['gbps']} GB/s", file=sys.stderr, flush=True)
+        del xd, xf, exact
+    print(json.dumps({"quality": records, "seed": seed, "data": "synthetic"}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,6 +206,9 @@ def main() -> int:
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the CPU oracle (profiling runs)")
+    ap.add_argument("--quality", action="store_true",
+                    help="instead of the benchmark: error (MSE) of both stages and throughput for "
+                         "every block size and width of the sweep and for the five workloads")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -117,6 +222,9 @@ def main() -> int:
 
     import bit_activation_compression_amd as fc
     import synth
+
+    if args.quality:
+        return quality_report(args.seed)
 
     w = synth.workload(args.workload)
     R, T, H, bits, group = w.R, w.T, w.H, w.bits, w.group
