@@ -71,14 +71,17 @@ def k1_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic() -> float | None:
+def measured_traffic(workload: str) -> float | None:
     """HBM bytes per K1 launch from the committed rocprofv3 counter summary, if it
-    was taken on the current K1 source; None otherwise."""
+    was taken on this workload and on the current K1 source; None otherwise."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     txt = open(TRAFFIC_FILE).read()
+    m_w = re.search(r"^workload:\s*(\S+)", txt, re.M)
     m_src = re.search(r"^k1_source_sha256_16:\s*(\S+)", txt, re.M)
     m_b = re.search(r"^k1_hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    if not m_w or m_w.group(1) != workload:
+        return None
     if not m_src or not m_b or m_src.group(1) != k1_source_hash():
         return None
     return float(m_b.group(1))
@@ -341,7 +344,7 @@ def main() -> int:
     value = mb["total"] / (ms_per_step * 1e-3) / 1e9
     k1_avg_ms = float(k1_ms.mean())
     k1_gbps = mb["k1"] / (k1_avg_ms * 1e-3) / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic(w.name)
 
     cpu = None
     if not args.no_cpu_baseline:
