@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
             L.ref_quantize_f32.argtypes = [P, ctypes.c_size_t, I, I, P, P, P]
             L.ref_sum_uncompressed.restype = I
             L.ref_sum_uncompressed.argtypes = [P, I, I, I, I, P]
+            L.ref_dequantize_residual.restype = I
+            L.ref_dequantize_residual.argtypes = [P, P, P, I, I, I, I, I, P, P]
             for name in ("ref_half_to_float_n", "ref_bf16_to_float_n",
                          "ref_float_to_half_n", "ref_float_to_bf16_n"):
                 fn = getattr(L, name)
@@ -224,4 +226,17 @@ def sum_uncompressed(x: np.ndarray, dtype: str) -> np.ndarray:
     R, T, H = x.shape
     out = np.zeros((T, H), dtype=np.uint16)
     _check(lib().ref_sum_uncompressed(_p(x), _DT[dtype], R, T, H, _p(out)), "sum_uncompressed")
+    return out
+
+
+def dequantize_residual(codes2, s2, z2, T: int, H: int, bits: int, group2: int, dtype: str,
+                        residual: np.ndarray) -> np.ndarray:
+    """Stage-2 payload and residual [T, H] 16-bit -> residual + all-reduce result, 16-bit."""
+    codes2 = np.ascontiguousarray(codes2, dtype=np.uint8)
+    s2 = np.ascontiguousarray(s2, dtype=np.uint16)
+    z2 = np.ascontiguousarray(z2, dtype=np.uint16)
+    residual = np.ascontiguousarray(residual, dtype=np.uint16)
+    out = np.zeros((T, H), dtype=np.uint16)
+    _check(lib().ref_dequantize_residual(_p(codes2), _p(s2), _p(z2), T, H, bits, group2,
+                                         _DT[dtype], _p(residual), _p(out)), "dequantize_residual")
     return out

@@ -458,3 +458,34 @@ int ref_sum_uncompressed(const uint16_t *x, int dtype, int R, int T, int H, uint
     }
     return REF_OK;
 }
+
+/*
+ * The final dequantize followed by the residual add of the transformer block
+ * (Figure 3: each attention and MLP output leaves the block through the
+ * all-reduce and is added to the residual stream). Reading taken here: the
+ * all-reduce result is first rounded to the model dtype, exactly as the
+ * separate dequantize returns it, and then added to the residual in binary32
+ * and rounded once more to the dtype -- the result the two separate steps
+ * give, so that fusing them changes only where the work is done.
+ *   codes2, s2, z2 [T][H] payload, residual [T][H] 16-bit -> out [T][H] 16-bit
+ */
+int ref_dequantize_residual(const uint8_t *codes2, const uint16_t *s2, const uint16_t *z2,
+                            int T, int H, int bits, int group2, int dtype,
+                            const uint16_t *residual, uint16_t *out)
+{
+    if (bits != 4 && bits != 8)
+        return REF_ERR_BITS;
+    if (T < 0 || H < 1 || group2 < 2 || group2 % 2 != 0 || H % group2 != 0)
+        return REF_ERR_SHAPE;
+    const int G2 = H / group2;
+    for (int t = 0; t < T; ++t) {
+        for (int h = 0; h < H; ++h) {
+            size_t e = (size_t)t * H + h;
+            size_t m = (size_t)t * G2 + (size_t)(h / group2);
+            uint16_t a = narrow(dequant(get_code(codes2, e, bits), s2[m], z2[m]), dtype);
+            float sum = widen(residual[e], dtype) + widen(a, dtype);
+            out[e] = narrow(sum, dtype);
+        }
+    }
+    return REF_OK;
+}

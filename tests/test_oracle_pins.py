@@ -568,3 +568,59 @@ def test_mixed_widths_mse_between_uniform_widths():
             mse[b1, b2] = float(np.mean((o - exact) ** 2))
     assert mse[4, 4] > mse[4, 8] > mse[8, 8]
     assert mse[4, 4] > mse[8, 4] > mse[8, 8]
+
+
+# ---------------------------------------------------------------------------
+# the final dequantize fused with the residual add (Figure 3's block)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fixture", ["residual_add_f16.txt", "residual_add_bf16.txt"])
+def test_residual_add_rounds_the_allreduce_result_first(fixture):
+    fx = _read_fixture(fixture)
+    bits, group, dt = int(fx["bits"][0]), int(fx["group"][0]), fx["dtype"][0]
+    codes = np.array([[int(v) for v in fx["codes"]]], dtype=np.uint8)
+    s = np.array([[int(fx["s_bits"][0], 16)]], dtype=np.uint16)
+    z = np.array([[int(fx["z_bits"][0], 16)]], dtype=np.uint16)
+    res = np.array([[int(v, 16) for v in fx["residual_bits"]]], dtype=np.uint16)
+    a, _ = oracle.dequantize(codes, s, z, 1, group, bits, group, dt)
+    assert list(a[0]) == [int(v, 16) for v in fx["a_bits"]]
+    out = oracle.dequantize_residual(codes, s, z, 1, group, bits, group, dt, res)
+    assert list(out[0]) == [int(v, 16) for v in fx["out_bits"]]
+
+
+def _payload_and_residual(dtype: str, bits: int, seed: int):
+    w = synth.workload("tiny").with_(dtype=dtype, bits=bits, T=16, H=512, R=4, group=128)
+    x = synth.operands(w, seed)
+    ref = oracle.allreduce(x, dtype, bits, w.group, want_f32=False)
+    # the residual stream: another seeded activation of the same shape
+    residual = synth.operands(w.with_(R=1, sigma=4.0), seed + 1000)[0]
+    return w, ref, residual
+
+
+@pytest.mark.parametrize("dtype", [oracle.F16, oracle.BF16])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_residual_add_equals_torch_add_of_the_two_steps(dtype, bits):
+    """Library routine: torch's CPU add of two 16-bit tensors (binary32 add, one
+    rounding) applied to the residual and the separately dequantized result."""
+    w, ref, residual = _payload_and_residual(dtype, bits, seed=5)
+    out = oracle.dequantize_residual(ref["codes2"], ref["s2"], ref["z2"], w.T, w.H, bits,
+                                     ref["group2"], dtype, residual)
+    tdt = torch.float16 if dtype == oracle.F16 else torch.bfloat16
+    a = torch.from_numpy(ref["out"].view(np.int16)).view(tdt)
+    r = torch.from_numpy(residual.view(np.int16)).view(tdt)
+    expect = (r + a).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(out, expect)
+
+
+@pytest.mark.parametrize("dtype", [oracle.F16, oracle.BF16])
+def test_residual_add_closed_forms(dtype):
+    w, ref, _ = _payload_and_residual(dtype, 4, seed=6)
+    args = (ref["codes2"], ref["s2"], ref["z2"], w.T, w.H, 4, ref["group2"], dtype)
+    a = ref["out"]
+    # +0 residual: the all-reduce result itself (as a value; -0 + +0 is +0)
+    out0 = oracle.dequantize_residual(*args, np.zeros_like(a))
+    widen = oracle.half_to_float if dtype == oracle.F16 else oracle.bf16_to_float
+    assert np.array_equal(widen(out0), widen(a))
+    # residual = -result: every element cancels to +0
+    neg = oracle.dequantize_residual(*args, a ^ np.uint16(0x8000))
+    assert np.all(neg == 0)
