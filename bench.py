@@ -341,6 +341,44 @@ def main() -> int:
     ref_pow = float((sum_out.float() ** 2).mean())
     del diff
 
+    # The residual add of the transformer block folded into the final step,
+    # against the same result computed unfused (dequantize, then torch's add).
+    xd0, c1, s1, z1, c2, s2, z2, out0 = sets[0]
+    residual = torch.empty((T, H), dtype=tdt, device=dev).normal_(0.0, 2.0)
+    res_out = torch.empty_like(residual)
+    tmp = torch.empty_like(residual)
+
+    def fused_res():
+        fc.fc_dequantize_residual(c2, s2, z2, T, H, bits, g2, residual, res_out, stream=stream)
+
+    def unfused_res():
+        fc.fc_dequantize(c2, s2, z2, T, H, bits, g2, tdt, tmp, stream=stream)
+        torch.add(residual, tmp, out=res_out)
+
+    def timed(fn, n=50):
+        for _ in range(5):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(n):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / n
+
+    pay2 = T * H * bits // 8 + T * (H // g2) * 4
+    res_fused_ms = timed(fused_res)
+    res_unfused_ms = timed(unfused_res)
+    residual_add = {
+        "fused_ms": round(res_fused_ms, 5),
+        "fused_bytes": pay2 + 2 * T * H * 2,
+        "fused_gbps": round((pay2 + 2 * T * H * 2) / (res_fused_ms * 1e-3) / 1e9, 1),
+        "unfused_ms": round(res_unfused_ms, 5),
+        "unfused_bytes": pay2 + 4 * T * H * 2,
+        "speedup": round(res_unfused_ms / res_fused_ms, 3),
+    }
+    del residual, res_out, tmp
+
     value = mb["total"] / (ms_per_step * 1e-3) / 1e9
     k1_avg_ms = float(k1_ms.mean())
     k1_gbps = mb["k1"] / (k1_avg_ms * 1e-3) / 1e9
@@ -395,6 +433,7 @@ def main() -> int:
                              "codec_mse_vs_uncompressed": mse,
                              "codec_snr_db": round(10 * np.log10(ref_pow / mse), 2) if mse > 0 else None},
         "link_bytes_per_rank": link_bytes(R, T, H, bits, group, g2),
+        "residual_add": residual_add,
         "roofline": {"bound": "hbm", "kernel": "k1_quantize", "achieved": round(k1_gbps, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(k1_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": mb["k1"],

@@ -24,7 +24,7 @@ __all__ = [
     "FcError", "lib", "library_path",
     "fc_quantize_groups", "fc_dequant_sum_requant", "fc_dequantize", "fc_allreduce_emulated",
     "fc_workspace_bytes", "fc_workspace_layout", "fc_stage2_group", "fc_status_string",
-    "fc_sum_uncompressed", "workspace_views", "EXPORTED_SYMBOLS",
+    "fc_sum_uncompressed", "fc_dequantize_residual", "workspace_views", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -37,6 +37,7 @@ EXPORTED_SYMBOLS = (
     "fc_workspace_bytes", "fc_workspace_layout", "fc_stage2_group", "fc_status_string",
     "fc_sum_uncompressed", "fc_dequant_sum_requant_mixed", "fc_allreduce_emulated_mixed",
     "fc_workspace_bytes_mixed", "fc_workspace_layout_mixed",
+    "fc_dequantize_residual", "fc_allreduce_emulated_residual",
 )
 
 _lock = threading.Lock()
@@ -67,9 +68,12 @@ def lib() -> ctypes.CDLL:
             L.fc_sum_uncompressed.argtypes = [P, I, I, I, I, P, P]
             L.fc_dequant_sum_requant_mixed.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P]
             L.fc_allreduce_emulated_mixed.argtypes = [P, I, I, I, I, I, I, I, P, P, Z, P]
+            L.fc_dequantize_residual.argtypes = [P, P, P, I, I, I, I, I, P, P, P]
+            L.fc_allreduce_emulated_residual.argtypes = [P, I, I, I, I, I, I, I, P, P, P, Z, P]
             for f in (L.fc_quantize_groups, L.fc_dequant_sum_requant, L.fc_dequantize,
                       L.fc_allreduce_emulated, L.fc_sum_uncompressed,
-                      L.fc_dequant_sum_requant_mixed, L.fc_allreduce_emulated_mixed):
+                      L.fc_dequant_sum_requant_mixed, L.fc_allreduce_emulated_mixed,
+                      L.fc_dequantize_residual, L.fc_allreduce_emulated_residual):
                 f.restype = I
             L.fc_workspace_bytes_mixed.argtypes = [I, I, I, I, I, I]
             L.fc_workspace_bytes_mixed.restype = Z
@@ -192,10 +196,28 @@ def fc_dequantize(codes2, s2, z2, T: int, H: int, bits: int, group2: int, dtype:
     return out
 
 
+def fc_dequantize_residual(codes2, s2, z2, T: int, H: int, bits: int, group2: int,
+                           residual: torch.Tensor, out=None, stream=None):
+    """Stage-2 payload + residual [T, H] -> out [T, H] = residual + dequantized result
+    (`out` may be `residual` itself for an in-place update)."""
+    for n, t in (("codes2", codes2), ("s2", s2), ("z2", z2), ("residual", residual)):
+        _dev_tensor(t, n)
+    dev = codes2.device
+    if out is None:
+        out = torch.empty((T, H), dtype=residual.dtype, device=dev)
+    if out.dtype != residual.dtype:
+        raise ValueError("out and residual must have the same dtype")
+    _check(lib().fc_dequantize_residual(_ptr(codes2), _ptr(s2), _ptr(z2), T, H, bits, group2,
+                                        _DTYPES[residual.dtype], _ptr(residual), _ptr(out),
+                                        _stream(stream, dev)), "fc_dequantize_residual")
+    return out
+
+
 def fc_allreduce_emulated(x: torch.Tensor, bits: int, group: int, out=None, workspace=None,
-                          stream=None, bits2: int | None = None):
+                          stream=None, bits2: int | None = None, residual=None):
     """x [R, T, H] -> out [T, H]: the whole emulated all-reduce (three kernels).
-    `bits` codes the reduce-scatter payload, `bits2` (default: the same) the all-gather one."""
+    `bits` codes the reduce-scatter payload, `bits2` (default: the same) the all-gather one.
+    With `residual` [T, H], out = residual + the all-reduce (the last kernel adds it)."""
     _dev_tensor(x, "x")
     bits2 = bits if bits2 is None else bits2
     R, T, H = x.shape
@@ -205,7 +227,15 @@ def fc_allreduce_emulated(x: torch.Tensor, bits: int, group: int, out=None, work
     if workspace is None:
         workspace = torch.empty(max(fc_workspace_bytes(R, T, H, bits, group, bits2), 1),
                                 dtype=torch.uint8, device=dev)
-    if bits2 == bits:
+    if residual is not None:
+        _dev_tensor(residual, "residual")
+        if residual.dtype != x.dtype or tuple(residual.shape) != (T, H):
+            raise ValueError("residual must be [T, H] of x's dtype")
+        st = lib().fc_allreduce_emulated_residual(_ptr(x), _DTYPES[x.dtype], R, T, H, bits, bits2,
+                                                  group, _ptr(residual), _ptr(out),
+                                                  _ptr(workspace), workspace.numel(),
+                                                  _stream(stream, dev))
+    elif bits2 == bits:
         st = lib().fc_allreduce_emulated(_ptr(x), _DTYPES[x.dtype], R, T, H, bits, group, _ptr(out),
                                          _ptr(workspace), workspace.numel(), _stream(stream, dev))
     else:

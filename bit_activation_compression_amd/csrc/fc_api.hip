@@ -77,6 +77,44 @@ fc_status check_shape2(int R, int T, int H, int bits1, int bits2, int group, int
     return FC_OK;
 }
 
+// The three launches of the emulated all-reduce; with_residual: the last one
+// adds the result to `residual`.
+fc_status allreduce_emulated(const void *x, fc_dtype dt, int R, int T, int H, int bits1, int bits2,
+                             int group, bool with_residual, const void *residual, void *out,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    int g2 = 0;
+    fc_status st = check_shape2(R, T, H, bits1, bits2, group, &g2);
+    if (st != FC_OK) return st;
+    if (dt != FC_F16 && dt != FC_BF16) return FC_ERR_DTYPE;
+    const uint64_t n = (uint64_t)T * (uint64_t)H;
+    st = with_residual ? check_ptrs(n, {x, residual, out, workspace})
+                       : check_ptrs(n, {x, out, workspace});
+    if (st != FC_OK) return st;
+    const Layout L = layout(R, T, H, bits1, bits2, group, g2);
+    if (n != 0 && workspace_bytes < L.total) return FC_ERR_WORKSPACE;
+    if (n == 0) return FC_OK;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    uint8_t *codes1 = ws + L.off[0];
+    uint16_t *s1 = reinterpret_cast<uint16_t *>(ws + L.off[1]);
+    uint16_t *z1 = reinterpret_cast<uint16_t *>(ws + L.off[2]);
+    uint8_t *codes2 = ws + L.off[3];
+    uint16_t *s2 = reinterpret_cast<uint16_t *>(ws + L.off[4]);
+    uint16_t *z2 = reinterpret_cast<uint16_t *>(ws + L.off[5]);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = from_hip(fc::launch_quantize(static_cast<const uint16_t *>(x), (int)dt, n * (uint64_t)R, bits1,
+                                      group, codes1, s1, z1, s));
+    if (st != FC_OK) return st;
+    st = from_hip(fc::launch_dequant_sum_requant(codes1, s1, z1, R, n, bits1, bits2, group, g2, codes2,
+                                                 s2, z2, s));
+    if (st != FC_OK) return st;
+    if (with_residual)
+        return from_hip(fc::launch_dequantize_residual(codes2, s2, z2, n, bits2, g2, (int)dt,
+                                                       static_cast<const uint16_t *>(residual),
+                                                       static_cast<uint16_t *>(out), s));
+    return from_hip(fc::launch_dequantize(codes2, s2, z2, n, bits2, g2, (int)dt,
+                                          static_cast<uint16_t *>(out), s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,32 +169,31 @@ fc_status fc_dequantize(const uint8_t *codes2, const uint16_t *s2, const uint16_
 fc_status fc_allreduce_emulated_mixed(const void *x, fc_dtype dt, int R, int T, int H, int bits1,
                                       int bits2, int group, void *out, void *workspace,
                                       size_t workspace_bytes, void *stream) {
-    int g2 = 0;
-    fc_status st = check_shape2(R, T, H, bits1, bits2, group, &g2);
-    if (st != FC_OK) return st;
+    return allreduce_emulated(x, dt, R, T, H, bits1, bits2, group, false, nullptr, out, workspace,
+                              workspace_bytes, stream);
+}
+
+fc_status fc_allreduce_emulated_residual(const void *x, fc_dtype dt, int R, int T, int H,
+                                         int bits1, int bits2, int group, const void *residual,
+                                         void *out, void *workspace, size_t workspace_bytes,
+                                         void *stream) {
+    return allreduce_emulated(x, dt, R, T, H, bits1, bits2, group, true, residual, out, workspace,
+                              workspace_bytes, stream);
+}
+
+fc_status fc_dequantize_residual(const uint8_t *codes2, const uint16_t *s2, const uint16_t *z2,
+                                 int T, int H, int bits, int group2, fc_dtype dt,
+                                 const void *residual, void *out, void *stream) {
+    if (bits != 4 && bits != 8) return FC_ERR_BITS;
+    if (T < 0 || H < 1 || !pow2_in_range(group2) || H % group2 != 0) return FC_ERR_SHAPE;
     if (dt != FC_F16 && dt != FC_BF16) return FC_ERR_DTYPE;
     const uint64_t n = (uint64_t)T * (uint64_t)H;
-    st = check_ptrs(n, {x, out, workspace});
-    if (st != FC_OK) return st;
-    const Layout L = layout(R, T, H, bits1, bits2, group, g2);
-    if (n != 0 && workspace_bytes < L.total) return FC_ERR_WORKSPACE;
-    if (n == 0) return FC_OK;
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    uint8_t *codes1 = ws + L.off[0];
-    uint16_t *s1 = reinterpret_cast<uint16_t *>(ws + L.off[1]);
-    uint16_t *z1 = reinterpret_cast<uint16_t *>(ws + L.off[2]);
-    uint8_t *codes2 = ws + L.off[3];
-    uint16_t *s2 = reinterpret_cast<uint16_t *>(ws + L.off[4]);
-    uint16_t *z2 = reinterpret_cast<uint16_t *>(ws + L.off[5]);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    st = from_hip(fc::launch_quantize(static_cast<const uint16_t *>(x), (int)dt, n * (uint64_t)R, bits1,
-                                      group, codes1, s1, z1, s));
-    if (st != FC_OK) return st;
-    st = from_hip(fc::launch_dequant_sum_requant(codes1, s1, z1, R, n, bits1, bits2, group, g2, codes2,
-                                                 s2, z2, s));
-    if (st != FC_OK) return st;
-    return from_hip(fc::launch_dequantize(codes2, s2, z2, n, bits2, g2, (int)dt,
-                                          static_cast<uint16_t *>(out), s));
+    fc_status st = check_ptrs(n, {codes2, s2, z2, residual, out});
+    if (st != FC_OK || n == 0) return st;
+    return from_hip(fc::launch_dequantize_residual(codes2, s2, z2, n, bits, group2, (int)dt,
+                                                   static_cast<const uint16_t *>(residual),
+                                                   static_cast<uint16_t *>(out),
+                                                   static_cast<hipStream_t>(stream)));
 }
 
 fc_status fc_allreduce_emulated(const void *x, fc_dtype dt, int R, int T, int H, int bits, int group,

@@ -25,6 +25,13 @@ hipError_t launch_dequantize(const uint8_t *codes2, const uint16_t *s2, const ui
                              uint64_t n, int bits, int group2, int dtype, uint16_t *out,
                              hipStream_t stream);
 
+// The same, added to a 16-bit residual [n] (may be the same array as out):
+// out = round(residual + round(q*s + z)).
+hipError_t launch_dequantize_residual(const uint8_t *codes2, const uint16_t *s2,
+                                      const uint16_t *z2, uint64_t n, int bits, int group2,
+                                      int dtype, const uint16_t *residual, uint16_t *out,
+                                      hipStream_t stream);
+
 // Uncompressed R-way sum over n = T*H positions of R operands laid out [R][n].
 hipError_t launch_sum(const uint16_t *x, int dtype, int R, uint64_t n, uint16_t *out,
                       hipStream_t stream);

@@ -129,6 +129,34 @@ fc_status fc_allreduce_emulated_mixed(const void *x, fc_dtype dt, int R, int T, 
                                       int bits2, int group, void *out, void *workspace,
                                       size_t workspace_bytes, void *stream);
 
+/*
+ * The final dequantize fused with the residual add that follows the
+ * all-reduce in the transformer block (Figure 3: the attention and the MLP
+ * outputs are all-reduced and added to the residual stream).
+ *   codes2 [T][H*bits/8], s2, z2 [T][H/group2], residual [T][H] in dt
+ *   ->  out [T][H] in dt,
+ *   out = round_half_even_to_dt(fp32(residual + a)),
+ *   a   = round_half_even_to_dt(fp32(q * s + z))   (what fc_dequantize writes)
+ * so the result is the one of fc_dequantize followed by a 16-bit add computed
+ * in binary32; the all-reduce result itself is not written. `out` may be the
+ * same pointer as `residual` (in-place update of the residual stream); any
+ * other overlap of the two is not supported. Same checks as fc_dequantize,
+ * plus residual (FC_ERR_NULL / FC_ERR_ALIGN).
+ */
+fc_status fc_dequantize_residual(const uint8_t *codes2, const uint16_t *s2, const uint16_t *z2,
+                                 int T, int H, int bits, int group2, fc_dtype dt,
+                                 const void *residual, void *out, void *stream);
+
+/*
+ * fc_allreduce_emulated_mixed whose last step is fc_dequantize_residual:
+ * out [T][H] = residual + the all-reduce of x, rounded as stated there. `out`
+ * may be the same pointer as `residual`.
+ */
+fc_status fc_allreduce_emulated_residual(const void *x, fc_dtype dt, int R, int T, int H,
+                                         int bits1, int bits2, int group, const void *residual,
+                                         void *out, void *workspace, size_t workspace_bytes,
+                                         void *stream);
+
 /* Workspace size and layout for the mixed-width pipeline (same slice order). */
 size_t fc_workspace_bytes_mixed(int R, int T, int H, int bits1, int bits2, int group);
 

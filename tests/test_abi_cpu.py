@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     L = fc.lib()
     names = _declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), n
     assert sorted(names) == sorted(fc.EXPORTED_SYMBOLS)
@@ -119,3 +119,22 @@ def test_other_entry_points_validate():
     need = fc.fc_workspace_bytes(2, 8, 256, 4, 128, bits2=8)
     assert L.fc_allreduce_emulated_mixed(FAKE, 0, 2, 8, 256, 4, 8, 128, FAKE, FAKE, need - 1, None) == 5
     assert L.fc_allreduce_emulated_mixed(None, 0, 2, 0, 256, 4, 8, 128, None, None, 0, None) == 0
+    # the residual add folded into the last step
+    assert L.fc_dequantize_residual(FAKE, FAKE, FAKE, 8, 256, 4, 96, 0, FAKE, FAKE, None) == 2
+    assert L.fc_dequantize_residual(FAKE, FAKE, FAKE, 8, 256, 6, 128, 0, FAKE, FAKE, None) == 3
+    assert L.fc_dequantize_residual(FAKE, FAKE, FAKE, 8, 256, 4, 128, 2, FAKE, FAKE, None) == 7
+    assert L.fc_dequantize_residual(FAKE, FAKE, FAKE, 8, 256, 4, 128, 0, None, FAKE, None) == 1
+    assert L.fc_dequantize_residual(FAKE, FAKE, FAKE, 8, 256, 4, 128, 0, MISALIGNED, FAKE,
+                                    None) == 4
+    assert L.fc_dequantize_residual(None, None, None, 0, 256, 4, 128, 0, None, None, None) == 0
+    need = fc.fc_workspace_bytes(2, 8, 256, 4, 128)
+    assert L.fc_allreduce_emulated_residual(FAKE, 0, 2, 8, 256, 4, 4, 128, None, FAKE, FAKE, need,
+                                            None) == 1
+    assert L.fc_allreduce_emulated_residual(FAKE, 0, 2, 8, 256, 4, 4, 128, MISALIGNED, FAKE, FAKE,
+                                            need, None) == 4
+    assert L.fc_allreduce_emulated_residual(FAKE, 0, 2, 8, 256, 4, 4, 128, FAKE, FAKE, FAKE,
+                                            need - 1, None) == 5
+    assert L.fc_allreduce_emulated_residual(FAKE, 0, 2, 8, 250, 4, 4, 128, FAKE, FAKE, FAKE, need,
+                                            None) == 2
+    assert L.fc_allreduce_emulated_residual(None, 0, 2, 0, 256, 4, 4, 128, None, None, None, 0,
+                                            None) == 0
