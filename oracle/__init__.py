@@ -7,8 +7,9 @@ this module compiles it with gcc when needed and marshals numpy arrays.
 
 Method: "Flash Communication: Reducing Tensor Parallelization Bottleneck for
 Fast Large Language Model Inference" (TL;DR; Abstract; Figure 4; Figure 5,
-right). Parity is pinned by `tests/test_oracle_pins.py` (closed forms, error
-bounds, brute force and library conversions); no function here is unpinned.
+right; Figure 3 for the transformer block around the all-reduce). Parity is
+pinned by `tests/test_oracle_pins.py` (closed forms, error bounds, brute force,
+integer arithmetic and library conversions); no function here is unpinned.
 """
 from __future__ import annotations
 
@@ -23,7 +24,8 @@ __all__ = [
     "build", "lib", "F16", "BF16", "OracleError",
     "half_to_float", "float_to_half", "bf16_to_float", "float_to_bf16",
     "quantize_groups", "dequant_sum_requant", "dequantize", "quantize_f32",
-    "allreduce", "stage2_group", "code_bytes", "sum_uncompressed",
+    "allreduce", "stage2_group", "code_bytes", "sum_uncompressed", "dequantize_residual",
+    "linear", "linear_quantize",
 ]
 
 F16 = "f16"
@@ -240,3 +242,36 @@ def dequantize_residual(codes2, s2, z2, T: int, H: int, bits: int, group2: int, 
     _check(lib().ref_dequantize_residual(_p(codes2), _p(s2), _p(z2), T, H, bits, group2,
                                          _DT[dtype], _p(residual), _p(out)), "dequantize_residual")
     return out
+
+
+def linear(a: np.ndarray, w: np.ndarray, dtype: str) -> np.ndarray:
+    """The row-parallel linear layer whose output each rank all-reduces (Figure 3:
+    the attention output projection and the MLP down projection; Figure 5, left,
+    names the two all-reduces o_proj and d_proj). Rank r holds its slice of the
+    layer input, a[r] [T, K], and the matching input columns of the weight,
+    w[r] [H, K] (a linear layer's [out, in] weight layout), and produces the
+    partial sum y[r] = a[r] @ w[r]^T [T, H] in the activation dtype.
+
+    Arithmetic: the dot products are taken in float64 (numpy's matmul, a library
+    step), rounded to binary32 -- the value a binary32 accumulator holds when
+    its accumulation is exact -- and then to the dtype, to nearest even.
+      a [R, T, K], w [R, H, K] uint16 bit patterns -> y [R, T, H] uint16 bit patterns
+    """
+    widen = half_to_float if dtype == F16 else bf16_to_float
+    narrow = float_to_half if dtype == F16 else float_to_bf16
+    A = widen(np.ascontiguousarray(a, dtype=np.uint16)).astype(np.float64)
+    W = widen(np.ascontiguousarray(w, dtype=np.uint16)).astype(np.float64)
+    if A.ndim != 3 or W.ndim != 3 or A.shape[0] != W.shape[0] or A.shape[2] != W.shape[2]:
+        raise OracleError(2, "linear")
+    y64 = np.matmul(A, W.transpose(0, 2, 1))
+    return narrow(y64.astype(np.float32))
+
+
+def linear_quantize(a: np.ndarray, w: np.ndarray, dtype: str, bits: int, group: int) -> dict:
+    """The linear layer followed by the quantization before the Reduce-Scatter
+    (Figure 3's block with Figure 5's first quantization): y = linear(a, w), then
+    the stage-1 codes of y exactly as quantize_groups gives them.
+      -> dict(y [R, T, H], codes1 [R, T, H*bits/8], s1, z1 [R, T, H/group])"""
+    y = linear(a, w, dtype)
+    codes1, s1, z1 = quantize_groups(y, dtype, bits, group)
+    return dict(y=y, codes1=codes1, s1=s1, z1=z1)

@@ -624,3 +624,70 @@ def test_residual_add_closed_forms(dtype):
     # residual = -result: every element cancels to +0
     neg = oracle.dequantize_residual(*args, a ^ np.uint16(0x8000))
     assert np.all(neg == 0)
+
+
+# ---------------------------------------------------------------------------
+# the row-parallel linear layer that produces the all-reduce operands (Figure 3)
+# ---------------------------------------------------------------------------
+
+def _dyadic(rng, shape, lo, hi, exp):
+    """Integers k in [lo, hi] scaled by 2^exp, as float64, and the integers."""
+    k = rng.integers(lo, hi + 1, size=shape).astype(np.int64)
+    return k, k.astype(np.float64) * 2.0 ** exp
+
+
+def _to_dtype_bits(v: np.ndarray, dtype: str) -> np.ndarray:
+    """Library rounding of float64 values exact in binary32: numpy's float16, torch's bfloat16."""
+    v32 = v.astype(np.float32)
+    assert np.array_equal(v32.astype(np.float64), v)
+    if dtype == oracle.F16:
+        return v32.astype(np.float16).view(np.uint16)
+    return torch.from_numpy(v32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", [oracle.F16, oracle.BF16])
+def test_linear_matches_integer_matmul(dtype):
+    """Integer arithmetic: with dyadic inputs every product and partial sum is an
+    integer multiple of 2^-9 below 2^24 of those units, so the layer output is
+    the int64 matmul, scaled, and rounded once to the dtype. Non-square shapes
+    and R > 1 catch a transposed or mismatched operand."""
+    rng = np.random.default_rng(21)
+    R, T, K, H = 3, 5, 24, 40
+    ka, af = _dyadic(rng, (R, T, K), -8, 8, -3)
+    kw, wf = _dyadic(rng, (R, H, K), -8, 8, -6)
+    kw[:, 7] *= 16                                 # an outlier output channel
+    wf[:, 7] *= 16
+    a = _to_dtype_bits(af, dtype)
+    w = _to_dtype_bits(wf, dtype)
+    exact = np.einsum("rtk,rhk->rth", ka, kw).astype(np.float64) * 2.0 ** -9
+    y = oracle.linear(a, w, dtype)
+    assert y.shape == (R, T, H)
+    assert np.array_equal(y, _to_dtype_bits(exact, dtype))
+
+
+def test_linear_permutation_weight_gathers_columns():
+    """Closed form: a weight with one 1 per output row (w[n][pi(n)] = 1) copies
+    input column pi(n) to output column n."""
+    rng = np.random.default_rng(22)
+    T, K = 6, 16
+    pi = rng.permutation(K)
+    a = synth.operands_from_values(rng.normal(size=(1, T, K)), oracle.BF16)
+    w = np.zeros((1, K, K), dtype=np.uint16)
+    w[0, np.arange(K), pi] = 0x3F80                # bfloat16 1.0
+    y = oracle.linear(a, w, oracle.BF16)
+    assert np.array_equal(y[0], a[0][:, pi])
+
+
+def test_linear_quantize_codes_are_those_of_the_layer_output():
+    rng = np.random.default_rng(23)
+    R, T, K, H = 2, 4, 32, 256
+    a = synth.operands_from_values(rng.normal(size=(R, T, K)), oracle.BF16)
+    w = synth.operands_from_values(rng.normal(size=(R, H, K)) * 0.05, oracle.BF16)
+    got = oracle.linear_quantize(a, w, oracle.BF16, 4, 128)
+    # the codes dequantize to within half a scale of the layer output (stage-1 bound)
+    y = oracle.bf16_to_float(got["y"]).astype(np.float64)
+    s = _hval(got["s1"]).repeat(128, axis=-1)
+    z = _hval(got["z1"]).repeat(128, axis=-1)
+    q = _unpack(got["codes1"], 4).astype(np.float64)
+    assert np.all(np.abs(q * s + z - y) <= s * (0.5 + 2.0 ** -14) + 2.0 ** -23 * np.abs(y)
+                  + np.maximum(0.0, z - y.reshape(R, T, -1, 128).min(-1).repeat(128, -1)))
