@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 METRIC = "achieved HBM GB/s (% of peak) for quant->dequant-sum-requant->dequant"
 WORKLOAD = "llama3_70b_prefill"
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16/fp16 matrix-core peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_llama3_70b_prefill_traffic.txt")
 K1_SOURCES = ("bit_activation_compression_amd/csrc/fc_quantize.hip",
               "bit_activation_compression_amd/csrc/fc_device.h")
@@ -207,6 +208,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--no-linear", action="store_true",
+                    help="skip the linear-layer leg (the GEMM with the quantizer in its epilogue)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the CPU oracle (profiling runs)")
     ap.add_argument("--quality", action="store_true",
@@ -379,6 +382,47 @@ def main() -> int:
     }
     del residual, res_out, tmp
 
+    # The row-parallel linear layer in front of the all-reduce (the attention
+    # output projection: K = H / R input features per rank) with the stage-1
+    # quantization in its epilogue, against the unfused pair (torch's batched
+    # GEMM writing y, then the stage-1 kernel reading it back).
+    linear = None
+    if not args.no_linear:
+        Kl = H // R
+        gen = torch.Generator(device=dev).manual_seed(args.seed)
+        la = torch.randn((R, T, Kl), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+        lw = (torch.randn((R, H, Kl), generator=gen, device=dev, dtype=torch.float32)
+              / Kl ** 0.5).to(tdt)
+        lwt = lw.transpose(1, 2).contiguous()           # [R, K, H] for torch.bmm
+        ly = torch.empty((R, T, H), dtype=tdt, device=dev)
+        lc, ls, lz = c1, s1, z1
+
+        def fused_lin():
+            fc.fc_linear_quantize(la, lw, bits, group, lc, ls, lz, stream=stream)
+
+        def gemm_only():
+            torch.bmm(la, lwt, out=ly)
+
+        def unfused_lin():
+            torch.bmm(la, lwt, out=ly)
+            fc.fc_quantize_groups(ly, bits, group, lc, ls, lz, stream=stream)
+
+        flops = 2.0 * R * T * H * Kl
+        lin_ms = timed(fused_lin, 20)
+        gemm_ms = timed(gemm_only, 20)
+        unf_ms = timed(unfused_lin, 20)
+        linear = {
+            "shape": {"R": R, "T": T, "K": Kl, "H": H},
+            "fused_ms": round(lin_ms, 4),
+            "fused_tflops": round(flops / (lin_ms * 1e-3) / 1e12, 1),
+            "fused_frac_of_mfma_peak": round(flops / (lin_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "torch_gemm_ms": round(gemm_ms, 4),
+            "torch_gemm_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
+            "unfused_ms": round(unf_ms, 4),
+            "speedup_vs_unfused": round(unf_ms / lin_ms, 3),
+        }
+        del la, lw, lwt, ly
+
     value = mb["total"] / (ms_per_step * 1e-3) / 1e9
     k1_avg_ms = float(k1_ms.mean())
     k1_gbps = mb["k1"] / (k1_avg_ms * 1e-3) / 1e9
@@ -434,6 +478,7 @@ def main() -> int:
                              "codec_snr_db": round(10 * np.log10(ref_pow / mse), 2) if mse > 0 else None},
         "link_bytes_per_rank": link_bytes(R, T, H, bits, group, g2),
         "residual_add": residual_add,
+        "linear_quantize": linear,
         "roofline": {"bound": "hbm", "kernel": "k1_quantize", "achieved": round(k1_gbps, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(k1_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": mb["k1"],

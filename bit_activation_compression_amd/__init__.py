@@ -24,7 +24,8 @@ __all__ = [
     "FcError", "lib", "library_path",
     "fc_quantize_groups", "fc_dequant_sum_requant", "fc_dequantize", "fc_allreduce_emulated",
     "fc_workspace_bytes", "fc_workspace_layout", "fc_stage2_group", "fc_status_string",
-    "fc_sum_uncompressed", "fc_dequantize_residual", "workspace_views", "EXPORTED_SYMBOLS",
+    "fc_sum_uncompressed", "fc_dequantize_residual", "fc_linear_quantize", "workspace_views",
+    "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +38,7 @@ EXPORTED_SYMBOLS = (
     "fc_workspace_bytes", "fc_workspace_layout", "fc_stage2_group", "fc_status_string",
     "fc_sum_uncompressed", "fc_dequant_sum_requant_mixed", "fc_allreduce_emulated_mixed",
     "fc_workspace_bytes_mixed", "fc_workspace_layout_mixed",
-    "fc_dequantize_residual", "fc_allreduce_emulated_residual",
+    "fc_dequantize_residual", "fc_allreduce_emulated_residual", "fc_linear_quantize",
 )
 
 _lock = threading.Lock()
@@ -70,7 +71,8 @@ def lib() -> ctypes.CDLL:
             L.fc_allreduce_emulated_mixed.argtypes = [P, I, I, I, I, I, I, I, P, P, Z, P]
             L.fc_dequantize_residual.argtypes = [P, P, P, I, I, I, I, I, P, P, P]
             L.fc_allreduce_emulated_residual.argtypes = [P, I, I, I, I, I, I, I, P, P, P, Z, P]
-            for f in (L.fc_quantize_groups, L.fc_dequant_sum_requant, L.fc_dequantize,
+            L.fc_linear_quantize.argtypes = [P, P, I, I, I, I, I, I, I, P, P, P, P, P]
+            for f in (L.fc_linear_quantize, L.fc_quantize_groups, L.fc_dequant_sum_requant, L.fc_dequantize,
                       L.fc_allreduce_emulated, L.fc_sum_uncompressed,
                       L.fc_dequant_sum_requant_mixed, L.fc_allreduce_emulated_mixed,
                       L.fc_dequantize_residual, L.fc_allreduce_emulated_residual):
@@ -194,6 +196,36 @@ def fc_dequantize(codes2, s2, z2, T: int, H: int, bits: int, group2: int, dtype:
     _check(lib().fc_dequantize(_ptr(codes2), _ptr(s2), _ptr(z2), T, H, bits, group2,
                                _DTYPES[out.dtype], _ptr(out), _stream(stream, dev)), "fc_dequantize")
     return out
+
+
+def fc_linear_quantize(a: torch.Tensor, w: torch.Tensor, bits: int, group: int, codes1=None,
+                       s1=None, z1=None, y=None, stream=None):
+    """Row-parallel linear layer of every rank with the stage-1 quantization in its
+    epilogue: a [R, T, K], w [R, H, K] (fp16/bf16) -> (codes1, s1, z1, y) for the
+    layer output y [R, T, H] = a @ w^T rounded to the dtype. y is written only when
+    a tensor (or True, to allocate one) is passed; otherwise None is returned."""
+    _dev_tensor(a, "a")
+    _dev_tensor(w, "w")
+    if a.dtype != w.dtype or a.dim() != 3 or w.dim() != 3 or a.shape[0] != w.shape[0] \
+            or a.shape[2] != w.shape[2]:
+        raise ValueError("a must be [R, T, K] and w [R, H, K] of one dtype")
+    R, T, K = a.shape
+    H = w.shape[1]
+    dev = a.device
+    if codes1 is None:
+        codes1 = torch.empty((R, T, H * bits // 8), dtype=torch.uint8, device=dev)
+    if s1 is None:
+        s1 = torch.empty((R, T, max(H // group, 0)), dtype=torch.uint16, device=dev)
+    if z1 is None:
+        z1 = torch.empty_like(s1)
+    if y is True:
+        y = torch.empty((R, T, H), dtype=a.dtype, device=dev)
+    elif y is not None:
+        _dev_tensor(y, "y")
+    _check(lib().fc_linear_quantize(_ptr(a), _ptr(w), _DTYPES[a.dtype], R, T, K, H, bits, group,
+                                    _ptr(codes1), _ptr(s1), _ptr(z1), _ptr(y),
+                                    _stream(stream, dev)), "fc_linear_quantize")
+    return codes1, s1, z1, y
 
 
 def fc_dequantize_residual(codes2, s2, z2, T: int, H: int, bits: int, group2: int,

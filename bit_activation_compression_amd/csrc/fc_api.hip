@@ -13,6 +13,11 @@ namespace {
 constexpr size_t kSliceAlign = 256;
 constexpr int kMinGroup = 8;
 constexpr int kMaxGroup = 8192;
+// fc_linear_quantize: channel tile, k stage and the largest group one lane
+// pair of its matrix-core tile holds
+constexpr int kLinearTileN = 256;
+constexpr int kLinearTileK = 64;
+constexpr int kLinearMaxGroup = 128;
 
 bool pow2_in_range(int g) { return g >= kMinGroup && g <= kMaxGroup && (g & (g - 1)) == 0; }
 
@@ -211,6 +216,27 @@ fc_status fc_sum_uncompressed(const void *x, fc_dtype dt, int R, int T, int H, v
     if (st != FC_OK || n == 0) return st;
     return from_hip(fc::launch_sum(static_cast<const uint16_t *>(x), (int)dt, R, n,
                                    static_cast<uint16_t *>(out), static_cast<hipStream_t>(stream)));
+}
+
+fc_status fc_linear_quantize(const void *a, const void *w, fc_dtype dt, int R, int T, int K, int H,
+                             int bits, int group, uint8_t *codes1, uint16_t *s1, uint16_t *z1,
+                             void *y, void *stream) {
+    int g2 = 0;
+    fc_status st = check_shape(R, T, H, bits, group, &g2);
+    if (st != FC_OK) return st;
+    if (K < kLinearTileK || K % kLinearTileK != 0 || H % kLinearTileN != 0 ||
+        group > kLinearMaxGroup)
+        return FC_ERR_SHAPE;
+    if (dt != FC_F16 && dt != FC_BF16) return FC_ERR_DTYPE;
+    const uint64_t n = (uint64_t)R * (uint64_t)T * (uint64_t)H;
+    st = check_ptrs(n, {a, w, codes1, s1, z1});
+    if (st != FC_OK || n == 0) return st;
+    if (y != nullptr && !aligned(y)) return FC_ERR_ALIGN;
+    return from_hip(fc::launch_linear_quantize(static_cast<const uint16_t *>(a),
+                                               static_cast<const uint16_t *>(w), (int)dt, R, T, K,
+                                               H, bits, group, codes1, s1, z1,
+                                               static_cast<uint16_t *>(y),
+                                               static_cast<hipStream_t>(stream)));
 }
 
 size_t fc_workspace_bytes_mixed(int R, int T, int H, int bits1, int bits2, int group) {

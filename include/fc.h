@@ -157,6 +157,28 @@ fc_status fc_allreduce_emulated_residual(const void *x, fc_dtype dt, int R, int 
                                          void *out, void *workspace, size_t workspace_bytes,
                                          void *stream);
 
+/*
+ * The row-parallel linear layer that produces the all-reduce operands, with
+ * the quantization before the Reduce-Scatter done in its epilogue (Figure 3:
+ * the attention output projection and the MLP down projection of every rank
+ * end in the all-reduce; Figure 5, left, names them o_proj and d_proj).
+ *   a  [R][T][K] in dt   rank r's slice of the layer input
+ *   w  [R][H][K] in dt   rank r's input columns of the weight ([out][in])
+ *   -> codes1, s1, z1 exactly as fc_quantize_groups gives them for
+ *      y [R][T][H], y[r] = round_half_even_to_dt(a[r] w[r]^T)
+ *   y  optional (NULL: not written): the layer output itself, in dt.
+ * The products are accumulated in binary32 on the matrix cores (the order of
+ * the accumulation is the hardware's), so y may differ from the exactly
+ * rounded product by the accumulation error; the codes are always those of
+ * the y this call computes (and writes, when y != NULL).
+ * Extra requirements (FC_ERR_SHAPE otherwise): K a positive multiple of 64,
+ * H a multiple of 256, group <= 128. Same checks as fc_quantize_groups
+ * otherwise; y, when given, 16-byte aligned.
+ */
+fc_status fc_linear_quantize(const void *a, const void *w, fc_dtype dt, int R, int T, int K, int H,
+                             int bits, int group, uint8_t *codes1, uint16_t *s1, uint16_t *z1,
+                             void *y, void *stream);
+
 /* Workspace size and layout for the mixed-width pipeline (same slice order). */
 size_t fc_workspace_bytes_mixed(int R, int T, int H, int bits1, int bits2, int group);
 

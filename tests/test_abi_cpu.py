@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     L = fc.lib()
     names = _declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
     assert sorted(names) == sorted(fc.EXPORTED_SYMBOLS)
@@ -138,3 +138,14 @@ def test_other_entry_points_validate():
                                             None) == 2
     assert L.fc_allreduce_emulated_residual(None, 0, 2, 0, 256, 4, 4, 128, None, None, None, 0,
                                             None) == 0
+    # the linear layer with the stage-1 quantization in its epilogue
+    LQ = L.fc_linear_quantize
+    assert LQ(FAKE, FAKE, 1, 4, 8, 2000, 8192, 4, 128, FAKE, FAKE, FAKE, None, None) == 2  # K % 64
+    assert LQ(FAKE, FAKE, 1, 4, 8, 2048, 8320, 4, 128, FAKE, FAKE, FAKE, None, None) == 2  # H % 256
+    assert LQ(FAKE, FAKE, 1, 4, 8, 2048, 8192, 4, 256, FAKE, FAKE, FAKE, None, None) == 2  # group
+    assert LQ(FAKE, FAKE, 1, 4, 8, 0, 8192, 4, 128, FAKE, FAKE, FAKE, None, None) == 2     # K = 0
+    assert LQ(FAKE, FAKE, 1, 4, 8, 2048, 8192, 6, 128, FAKE, FAKE, FAKE, None, None) == 3
+    assert LQ(FAKE, FAKE, 2, 4, 8, 2048, 8192, 4, 128, FAKE, FAKE, FAKE, None, None) == 7
+    assert LQ(FAKE, None, 1, 4, 8, 2048, 8192, 4, 128, FAKE, FAKE, FAKE, None, None) == 1
+    assert LQ(FAKE, FAKE, 1, 4, 8, 2048, 8192, 4, 128, FAKE, FAKE, FAKE, MISALIGNED, None) == 4
+    assert LQ(None, None, 1, 4, 0, 2048, 8192, 4, 128, None, None, None, None, None) == 0
