@@ -382,46 +382,54 @@ def main() -> int:
     }
     del residual, res_out, tmp
 
-    # The row-parallel linear layer in front of the all-reduce (the attention
-    # output projection: K = H / R input features per rank) with the stage-1
-    # quantization in its epilogue, against the unfused pair (torch's batched
-    # GEMM writing y, then the stage-1 kernel reading it back).
+    # The row-parallel linear layers in front of the all-reduce (Figure 5,
+    # left: the attention output projection o_proj, K = H / R input features
+    # per rank, and the MLP down projection d_proj, K = ffn / R) with the
+    # stage-1 quantization in the GEMM's epilogue, against the unfused pair
+    # (torch's batched GEMM writing y, then the stage-1 kernel reading it back).
     linear = None
     if not args.no_linear:
-        Kl = H // R
-        gen = torch.Generator(device=dev).manual_seed(args.seed)
-        la = torch.randn((R, T, Kl), generator=gen, device=dev, dtype=torch.float32).to(tdt)
-        lw = (torch.randn((R, H, Kl), generator=gen, device=dev, dtype=torch.float32)
-              / Kl ** 0.5).to(tdt)
-        lwt = lw.transpose(1, 2).contiguous()           # [R, K, H] for torch.bmm
-        ly = torch.empty((R, T, H), dtype=tdt, device=dev)
-        lc, ls, lz = c1, s1, z1
+        linear = {}
+        shapes = [("o_proj", H // R)] + ([("d_proj", w.ffn // R)] if w.ffn else [])
+        for name, Kl in shapes:
+            if Kl % 32 or H % 256 or group > 128:
+                continue
+            gen = torch.Generator(device=dev).manual_seed(args.seed)
+            la = torch.randn((R, T, Kl), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+            lw = (torch.randn((R, H, Kl), generator=gen, device=dev, dtype=torch.float32)
+                  / Kl ** 0.5).to(tdt)
+            lwt = lw.transpose(1, 2).contiguous()           # [R, K, H] for torch.bmm
+            ly = torch.empty((R, T, H), dtype=tdt, device=dev)
 
-        def fused_lin():
-            fc.fc_linear_quantize(la, lw, bits, group, lc, ls, lz, stream=stream)
+            def fused_lin():
+                fc.fc_linear_quantize(la, lw, bits, group, c1, s1, z1, stream=stream)
 
-        def gemm_only():
-            torch.bmm(la, lwt, out=ly)
+            def gemm_only():
+                torch.bmm(la, lwt, out=ly)
 
-        def unfused_lin():
-            torch.bmm(la, lwt, out=ly)
-            fc.fc_quantize_groups(ly, bits, group, lc, ls, lz, stream=stream)
+            def unfused_lin():
+                torch.bmm(la, lwt, out=ly)
+                fc.fc_quantize_groups(ly, bits, group, c1, s1, z1, stream=stream)
 
-        flops = 2.0 * R * T * H * Kl
-        lin_ms = timed(fused_lin, 20)
-        gemm_ms = timed(gemm_only, 20)
-        unf_ms = timed(unfused_lin, 20)
-        linear = {
-            "shape": {"R": R, "T": T, "K": Kl, "H": H},
-            "fused_ms": round(lin_ms, 4),
-            "fused_tflops": round(flops / (lin_ms * 1e-3) / 1e12, 1),
-            "fused_frac_of_mfma_peak": round(flops / (lin_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "torch_gemm_ms": round(gemm_ms, 4),
-            "torch_gemm_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
-            "unfused_ms": round(unf_ms, 4),
-            "speedup_vs_unfused": round(unf_ms / lin_ms, 3),
-        }
-        del la, lw, lwt, ly
+            flops = 2.0 * R * T * H * Kl
+            n_it = max(3, min(20, int(2e13 / flops)))
+            lin_ms = timed(fused_lin, n_it)
+            gemm_ms = timed(gemm_only, n_it)
+            unf_ms = timed(unfused_lin, n_it)
+            tf = flops / (lin_ms * 1e-3) / 1e12
+            linear[name] = {
+                "shape": {"R": R, "T": T, "K": Kl, "H": H},
+                "fused_ms": round(lin_ms, 4),
+                "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                             "timing": f"HIP events around {n_it} back-to-back launches"},
+                "torch_gemm_ms": round(gemm_ms, 4),
+                "torch_gemm_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
+                "unfused_ms": round(unf_ms, 4),
+                "speedup_vs_unfused": round(unf_ms / lin_ms, 3),
+            }
+            del la, lw, lwt, ly
+            torch.cuda.empty_cache()
 
     value = mb["total"] / (ms_per_step * 1e-3) / 1e9
     k1_avg_ms = float(k1_ms.mean())

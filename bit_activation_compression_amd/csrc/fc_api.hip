@@ -16,7 +16,7 @@ constexpr int kMaxGroup = 8192;
 // fc_linear_quantize: channel tile, k stage and the largest group one lane
 // pair of its matrix-core tile holds
 constexpr int kLinearTileN = 256;
-constexpr int kLinearTileK = 64;
+constexpr int kLinearTileK = 32;
 constexpr int kLinearMaxGroup = 128;
 
 bool pow2_in_range(int g) { return g >= kMinGroup && g <= kMaxGroup && (g & (g - 1)) == 0; }

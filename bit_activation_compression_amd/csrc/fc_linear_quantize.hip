@@ -24,12 +24,11 @@
 //     group (<= 128 consecutive channels of one token) lies in one lane pair
 //     (lane, lane ^ 32), half in each, and its minimum and maximum need one
 //     v_permlane32_swap after the in-lane reduction;
-//   - K is walked in stages of 64: both 256 x 64 operand tiles are staged in
-//     LDS (double-buffered, 128 KiB) straight from global memory
-//     (global_load_lds), each row's eight 16-byte chunks placed at
-//     chunk ^ (row % 8) so that the fragment reads (32 rows x one chunk) are
-//     free of bank conflicts; the next stage's loads are in flight while the
-//     matrix cores work on the current one;
+//   - K is walked in stages of 32: both 256 x 32 operand tiles are staged in
+//     an LDS ring of 4 stages (128 KiB) straight from global memory
+//     (global_load_lds), three stages ahead of the matrix cores; each 64-byte
+//     row's four 16-byte chunks are rotated by (row / 4) % 4 so that the
+//     fragment reads (32 rows x one chunk) are free of bank conflicts;
 //   - workgroups are numbered so that each XCD (its own L2) runs a contiguous
 //     run of tiles, ordered 4 token tiles x all channel tiles, so that
 //     concurrently running workgroups share their A and W stage tiles in L2.
@@ -47,7 +46,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTileN = 256;                 // output channels per workgroup
 constexpr int kTileT = 256;                 // tokens per workgroup
-constexpr int kTileK = 64;                  // k per LDS stage
+constexpr int kTileK = 32;                  // k per LDS stage
+constexpr int kStages = 4;                  // LDS ring; loads run kStages - 1 stages ahead
 constexpr int kWaveSpan = 128;              // channels (and tokens) per wave
 constexpr int kBlk = kWaveSpan / 32;        // 32 x 32 MFMA blocks per wave side
 constexpr int kStage = (kTileN + kTileT) * kTileK;   // 16-bit elements per stage
@@ -66,9 +66,34 @@ __device__ __forceinline__ f32x16 mfma(const u32x4 &a, const u32x4 &b, const f32
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// Element offset of chunk c of staged row `row`.
+// Element offset of 16-byte chunk c (0..3) of staged row `row` (64 bytes):
+// chunks are rotated by (row / 4) % 4, so that any 8 consecutive rows read at
+// one chunk index cover all 64 LDS banks once.
 __device__ __forceinline__ uint32_t lds_at(uint32_t row, uint32_t c) {
-    return row * kTileK + ((c ^ (row & 7u)) << 3);
+    return row * kTileK + ((c ^ ((row >> 2) & 3u)) << 3);
+}
+
+// s_waitcnt until at most N vector-memory operations of this wave are
+// outstanding and all of its LDS operations are done (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt left at its maximum, lgkmcnt 0). The LDS part
+// makes sure this wave's reads of a buffer have completed before the barrier
+// after which another wave may refill it.
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier that orders memory accesses for the compiler but, unlike
+// __syncthreads, does not wait for this wave's outstanding loads: the staging
+// loads of later stages stay in flight (their completion is waited for with
+// wait_loads before the barrier that publishes them).
+__device__ __forceinline__ void barrier_keep_loads() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Codes of 4 consecutive channels, same arithmetic as the stage-1 quantizer:
@@ -137,7 +162,7 @@ void linear_quantize_kernel(
     int tiles_t, int tiles_n, int total, uint8_t *__restrict__ codes, uint16_t *__restrict__ s,
     uint16_t *__restrict__ z, uint16_t *__restrict__ y) {
     static_assert(G >= 8 && G <= kWaveSpan && (G & (G - 1)) == 0, "group of 8..128 channels");
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * kStage];
 
     const uint32_t tid = __builtin_amdgcn_workitem_id_x();
     const int lane = (int)(tid & 63u);
@@ -166,29 +191,31 @@ void linear_quantize_kernel(
 
     // Staging, global -> LDS directly (global_load_lds_dwordx4: lane i's 16
     // bytes land at the instruction's LDS base + 16 i). One instruction fills
-    // 8 staged rows; lane i serves row i / 8 at chunk position i % 8, so it
-    // fetches the operand's chunk (i % 8) ^ (row % 8) -- the swizzle lds_at
-    // reads back. Wave w fills rows w*64 .. w*64+63 of both tiles (8
-    // instructions each). Token rows past the end re-read the last one.
-    const uint32_t lrow = (uint32_t)lane >> 3;                 // == row % 8
-    const uint32_t lchunk = ((uint32_t)lane & 7u) ^ lrow;
+    // 16 staged rows of 64 bytes; lane i serves row i / 4 at chunk position
+    // i % 4, so it fetches the operand's chunk (i % 4) ^ ((row / 4) % 4) --
+    // the rotation lds_at reads back. Wave w fills rows w*64 .. w*64+63 of
+    // both tiles (4 instructions each, 8 per stage). Token rows past the end
+    // re-read the last one.
+    constexpr int kLoadsPerStage = 8;            // per wave
+    const uint32_t lrow = (uint32_t)lane >> 2;   // row within the instruction's 16
+    const uint32_t lchunk = ((uint32_t)lane & 3u) ^ ((lrow >> 2) & 3u);
     const uint32_t wrow0 = (uint32_t)wave * 64u;
     const char *Wc = reinterpret_cast<const char *>(Wb);
     const char *Ac = reinterpret_cast<const char *>(Ab);
-    uint32_t w_off[8], a_off[8];
+    uint32_t w_off[4], a_off[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t row = wrow0 + 8u * j + lrow;
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t row = wrow0 + 16u * j + lrow;
         w_off[j] = row * rowb + lchunk * 16u;
         a_off[j] = (row < last_t ? row : last_t) * rowb + lchunk * 16u;
     }
-    auto stage_in = [&](int kt, int buf) {
+    auto stage_in = [&](int kt) {
         const uint32_t kb = (uint32_t)kt * (kTileK * 2);
-        uint16_t *sw = lds + buf * kStage;
+        uint16_t *sw = lds + (kt % kStages) * kStage;
         uint16_t *sa = sw + kTileN * kTileK;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t lrow0 = (wrow0 + 8u * j) * kTileK;   // wave-uniform
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t lrow0 = (wrow0 + 16u * j) * kTileK;   // wave-uniform
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void *)(Wc + w_off[j] + kb),
                 (__attribute__((address_space(3))) void *)(sw + lrow0), 16, 0, 0);
@@ -200,8 +227,9 @@ void linear_quantize_kernel(
 
     // fragment reads: row (block base + lane % 32), chunk 2 ks + lane / 32
     const uint32_t frow = (uint32_t)lane & 31u, fhalf = (uint32_t)lane >> 5;
-    auto frags = [&](const uint16_t *sw, const uint16_t *sa, int ks, u32x4 (&fw)[kBlk],
-                     u32x4 (&fa)[kBlk]) {
+    auto frags = [&](int kt, int ks, u32x4 (&fw)[kBlk], u32x4 (&fa)[kBlk]) {
+        const uint16_t *sw = lds + (kt % kStages) * kStage;
+        const uint16_t *sa = sw + kTileN * kTileK;
         const uint32_t c = 2u * ks + fhalf;
 #pragma unroll
         for (int b = 0; b < kBlk; ++b) {
@@ -216,13 +244,14 @@ void linear_quantize_kernel(
 #pragma unroll
         for (int b = 0; b < kBlk; ++b) acc[a][b] = f32x16{};
 
-    // One stage = 4 steps of k = 16, 16 MFMAs each. Software pipeline: the
-    // next stage's staging loads go out at the start; each step's MFMAs are
-    // interleaved with the LDS reads of the next step's fragments; the
-    // workgroup barrier that publishes the next stage sits before the last
-    // step, whose MFMAs then overlap the reads of the next stage's first
-    // fragments (every read of the current buffer has been issued and waited
-    // for by then, so the following stage may refill it).
+    // One stage = 2 steps of k = 16, 16 MFMAs each, over an LDS ring of
+    // kStages buffers. At stage kt the loads of stage kt + kStages - 1 go out
+    // (into the buffer stage kt - 1 used); step 0's MFMAs overlap the reads of
+    // step 1's fragments; then this wave waits until its loads of stage kt + 1
+    // have landed (the later stages' loads stay in flight) and the workgroup
+    // barrier publishes stage kt + 1; step 1's MFMAs overlap the reads of its
+    // first fragments. Every read of a buffer happens before the barrier that
+    // precedes its refill.
     u32x4 fw[2][kBlk], fa[2][kBlk];
     auto step = [&](int ks) {
 #pragma unroll
@@ -231,7 +260,7 @@ void linear_quantize_kernel(
             for (int tb = 0; tb < kBlk; ++tb)
                 acc[nb][tb] = mfma<DT>(fw[ks & 1][nb], fa[ks & 1][tb], acc[nb][tb]);
     };
-    // 16 MFMAs interleaved with 8 LDS reads and optionally 8 staging loads
+    // 16 MFMAs interleaved with 8 LDS reads and optionally the 8 staging loads
     auto interleave = [&](bool lds_reads, bool vmem) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -242,61 +271,71 @@ void linear_quantize_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto stage = [&](int kt, auto next_tag) {
-        constexpr bool NEXT = decltype(next_tag)::value;
-        const int buf = kt & 1;
-        const uint16_t *sw = lds + buf * kStage;
-        const uint16_t *sa = sw + kTileN * kTileK;
-        if constexpr (NEXT) stage_in(kt + 1, buf ^ 1);
-        frags(sw, sa, 1, fw[1], fa[1]);
+    // ISSUE: stage kt + kStages - 1 exists; PEND: stages issued after kt + 1
+    // (0, 1 or 2 -- they may stay in flight); LAST: no stage follows
+    auto stage = [&](int kt, auto issue_tag, auto pend_tag, auto last_tag) {
+        constexpr bool ISSUE = decltype(issue_tag)::value;
+        constexpr int PEND = decltype(pend_tag)::value;
+        constexpr bool LAST = decltype(last_tag)::value;
+        if constexpr (ISSUE) stage_in(kt + kStages - 1);
+        frags(kt, 1, fw[1], fa[1]);
         step(0);
-        interleave(true, NEXT);
-        frags(sw, sa, 2, fw[0], fa[0]);
-        step(1);
-        interleave(true, NEXT);
-        frags(sw, sa, 3, fw[1], fa[1]);
-        step(2);
-        interleave(true, false);
-        if constexpr (NEXT) {
-            __builtin_amdgcn_s_waitcnt(0);   // this wave's staging loads have landed
-            __syncthreads();
-            const uint16_t *nw = lds + (buf ^ 1) * kStage;
-            frags(nw, nw + kTileN * kTileK, 0, fw[0], fa[0]);
+        interleave(true, ISSUE);
+        if constexpr (!LAST) {
+            wait_loads<PEND * kLoadsPerStage>();
+            barrier_keep_loads();
+            frags(kt + 1, 0, fw[0], fa[0]);
         }
-        step(3);
-        interleave(NEXT, false);
+        step(1);
+        interleave(!LAST, false);
     };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
 
     const int KT = K / kTileK;
-    stage_in(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    frags(lds, lds + kTileN * kTileK, 0, fw[0], fa[0]);
-    for (int kt = 0; kt + 1 < KT; ++kt) stage(kt, std::true_type{});
-    stage(KT - 1, std::false_type{});
+    // prologue: the first min(KT, kStages - 1) stages; wait for stage 0
+    stage_in(0);
+    if (KT > 1) stage_in(1);
+    if (KT > 2) stage_in(2);
+    if (KT > 2) wait_loads<2 * kLoadsPerStage>();
+    else if (KT > 1) wait_loads<kLoadsPerStage>();
+    else wait_loads<0>();
+    barrier_keep_loads();
+    frags(0, 0, fw[0], fa[0]);
+    for (int kt = 0; kt + 3 < KT; ++kt) stage(kt, T_{}, P2{}, F_{});
+    if (KT >= 3) stage(KT - 3, F_{}, P1{}, F_{});
+    if (KT >= 2) stage(KT - 2, F_{}, P0{}, F_{});
+    stage(KT - 1, F_{}, P0{}, T_{});
 
     // ---- epilogue: round to the dtype, quantize per (token, group) ----
     // Run j = 4 nb + m of a lane holds channels nb*32 + 8m + 4*(lane/32) + 0..3
     // of the wave's span (accumulator entries 4m..4m+3 of block nb); a group
     // of G channels is RG = G/8 consecutive runs of each lane of the pair.
+    // Codes, scales and zeros of the whole tile are first gathered in LDS (the
+    // operand buffers are free by then) and then written out row by row in
+    // 16-byte pieces: a token row of the tile is one contiguous run of codes.
     constexpr int RG = G / 8;
+    constexpr int kCodeRow = kTileN * BITS / 8;      // code bytes of a tile row
+    constexpr int kCodePitch = kCodeRow + 16;        // padded (spreads LDS banks)
+    constexpr int kMetaRow = kTileN / G * 2;         // bytes of s (or z) of a tile row
+    static_assert(kTileT * (kCodePitch + 2 * kMetaRow) <= kStages * kStage * 2, "tile fits in LDS");
+    uint8_t *lc = reinterpret_cast<uint8_t *>(lds);
+    uint8_t *lsz = lc + kTileT * kCodePitch;         // s rows, then z rows
     const int Hg = H / G;
     const uint32_t h4 = 4u * fhalf;
-    // wave-uniform bases of this wave's first token row; per-lane 32-bit offsets
-    const uint32_t crow_b = (uint32_t)H * BITS / 8;           // code bytes per token row
-    const uint32_t lane_c = frow * crow_b;
     const uint32_t lane_y = frow * (uint32_t)H * 2u;
-    const uint32_t lane_m = frow * (uint32_t)Hg * 2u;
+    __syncthreads();   // every wave has read its last operand fragments
 #pragma unroll
     for (int tb = 0; tb < kBlk; ++tb) {
-        const int trow0 = t0 + wt * kWaveSpan + tb * 32;   // wave-uniform
+        const uint32_t tl = (uint32_t)(wt * kWaveSpan + tb * 32) + frow;   // token in the tile
+        const int trow0 = t0 + wt * kWaveSpan + tb * 32;
         const bool live = trow0 + (int)frow < T;
-        const size_t row0 = (size_t)r * T + (size_t)trow0;
-        const size_t col0 = (size_t)(n0 + wn * kWaveSpan);
-        uint8_t *cb = codes + (row0 * (size_t)H + col0) * BITS / 8;
-        uint16_t *yb = y ? y + row0 * (size_t)H + col0 : nullptr;
-        uint16_t *sb = s + row0 * (size_t)Hg + col0 / G;
-        uint16_t *zb = z + row0 * (size_t)Hg + col0 / G;
+        uint16_t *yb = y ? y + ((size_t)r * T + (size_t)trow0) * (size_t)H +
+                               (size_t)(n0 + wn * kWaveSpan)
+                         : nullptr;
 #pragma unroll
         for (int gi = 0; gi < kWaveSpan / G; ++gi) {
             // the group's values rounded to the dtype: packed pairs (yw) and
@@ -323,22 +362,54 @@ void linear_quantize_kernel(
             }
             pair_minmax(mn, mx);
             const GroupParams p = group_params<BITS>(mn, mx);
-            if (!live) continue;
 #pragma unroll
             for (int jj = 0; jj < RG; ++jj) {
                 const int j = gi * RG + jj;
-                const uint32_t ch = (uint32_t)((j / 4) * 32 + (j % 4) * 8) + h4;
+                const uint32_t ch = (uint32_t)((j / 4) * 32 + (j % 4) * 8) + h4;   // in the wave span
                 const uint32_t q = encode4<BITS>(yv[jj], p);
+                const uint32_t at = tl * kCodePitch + (wn * kWaveSpan + ch) * BITS / 8;
                 if constexpr (BITS == 8)
-                    stv<uint32_t, false>(cb, lane_c + ch, q);
+                    *reinterpret_cast<uint32_t *>(lc + at) = q;
                 else
-                    stv<uint16_t, false>(cb, lane_c + ch / 2, (uint16_t)q);
-                if (yb) stv<u32x2, false>(yb, lane_y + ch * 2u, u32x2{yw[jj][0], yw[jj][1]});
+                    *reinterpret_cast<uint16_t *>(lc + at) = (uint16_t)q;
+                if (yb && live) stv<u32x2, false>(yb, lane_y + ch * 2u, u32x2{yw[jj][0], yw[jj][1]});
             }
             if (fhalf == 0) {
-                stv<uint16_t, false>(sb, lane_m + 2u * gi, p.s16);
-                stv<uint16_t, false>(zb, lane_m + 2u * gi, p.z16);
+                const uint32_t m = tl * kMetaRow + (uint32_t)(wn * (kWaveSpan / G) + gi) * 2u;
+                *reinterpret_cast<uint16_t *>(lsz + m) = p.s16;
+                *reinterpret_cast<uint16_t *>(lsz + kTileT * kMetaRow + m) = p.z16;
             }
+        }
+    }
+    __syncthreads();
+
+    // write-out of the tile's live token rows
+    const int rows = min(kTileT, T - t0);
+    const size_t grow0 = (size_t)r * T + (size_t)t0;
+    uint8_t *cg = codes + (grow0 * (size_t)H + (size_t)n0) * BITS / 8;
+    const uint32_t cpitch = (uint32_t)H * BITS / 8;
+    constexpr int kCodeChunks = kCodeRow / 16;
+#pragma unroll
+    for (int i = 0; i < kTileT * kCodeChunks / kBlockThreads; ++i) {
+        const uint32_t id = (uint32_t)i * kBlockThreads + tid;
+        const uint32_t row = id / kCodeChunks, c = id % kCodeChunks;
+        if ((int)row < rows)
+            stv<u32x4, false>(cg, row * cpitch + c * 16u,
+                              *reinterpret_cast<const u32x4 *>(lc + row * kCodePitch + c * 16u));
+    }
+    uint16_t *sg = s + grow0 * (size_t)Hg + (size_t)(n0 / G);
+    uint16_t *zg = z + grow0 * (size_t)Hg + (size_t)(n0 / G);
+    const uint32_t mpitch = (uint32_t)Hg * 2u;
+    constexpr int kMetaWords = kMetaRow / 4;         // 4-byte pieces of a row
+#pragma unroll
+    for (int i = 0; i < (kTileT * kMetaWords + kBlockThreads - 1) / kBlockThreads; ++i) {
+        const uint32_t id = (uint32_t)i * kBlockThreads + tid;
+        const uint32_t row = id / kMetaWords, c = id % kMetaWords;
+        if ((int)row < rows) {
+            const uint32_t at = row * kMetaRow + c * 4u;
+            stv<uint32_t, false>(sg, row * mpitch + c * 4u, *reinterpret_cast<const uint32_t *>(lsz + at));
+            stv<uint32_t, false>(zg, row * mpitch + c * 4u,
+                                 *reinterpret_cast<const uint32_t *>(lsz + kTileT * kMetaRow + at));
         }
     }
 }

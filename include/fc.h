@@ -171,7 +171,7 @@ fc_status fc_allreduce_emulated_residual(const void *x, fc_dtype dt, int R, int 
  * the accumulation is the hardware's), so y may differ from the exactly
  * rounded product by the accumulation error; the codes are always those of
  * the y this call computes (and writes, when y != NULL).
- * Extra requirements (FC_ERR_SHAPE otherwise): K a positive multiple of 64,
+ * Extra requirements (FC_ERR_SHAPE otherwise): K a positive multiple of 32,
  * H a multiple of 256, group <= 128. Same checks as fc_quantize_groups
  * otherwise; y, when given, 16-byte aligned.
  */

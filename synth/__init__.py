@@ -58,6 +58,7 @@ class Workload:
     sigma: float = 1.0      # standard deviation of the normal draw
     outlier_frac: float = 0.0
     outlier_scale: float = 1.0
+    ffn: int = 0            # MLP intermediate size of the model (0: not a model shape)
 
     @property
     def n_outliers(self) -> int:
@@ -71,12 +72,13 @@ _BASE = {
     "tiny": Workload("tiny", R=2, T=8, H=256, dtype=F16, bits=8, group=128),
     "llama3_8b_prefill": Workload(
         "llama3_8b_prefill", R=4, T=8192, H=4096, dtype=F16, bits=4, group=128,
-        outlier_frac=0.01, outlier_scale=20.0),
+        outlier_frac=0.01, outlier_scale=20.0, ffn=14336),
     "llama3_70b_prefill": Workload(
         "llama3_70b_prefill", R=4, T=8192, H=8192, dtype=BF16, bits=4, group=128,
-        sigma=0.5, outlier_frac=0.005, outlier_scale=30.0),
+        sigma=0.5, outlier_frac=0.005, outlier_scale=30.0, ffn=28672),
     "decode": Workload(
-        "decode", R=8, T=64, H=8192, dtype=BF16, bits=4, group=128, dist="laplace"),
+        "decode", R=8, T=64, H=8192, dtype=BF16, bits=4, group=128, dist="laplace",
+        ffn=28672),
 }
 SWEEP_GROUPS = (4096, 1024, 512, 256, 128)
 SWEEP_BITS = (8, 4)

@@ -140,7 +140,7 @@ def test_other_entry_points_validate():
                                             None) == 0
     # the linear layer with the stage-1 quantization in its epilogue
     LQ = L.fc_linear_quantize
-    assert LQ(FAKE, FAKE, 1, 4, 8, 2000, 8192, 4, 128, FAKE, FAKE, FAKE, None, None) == 2  # K % 64
+    assert LQ(FAKE, FAKE, 1, 4, 8, 2000, 8192, 4, 128, FAKE, FAKE, FAKE, None, None) == 2  # K % 32
     assert LQ(FAKE, FAKE, 1, 4, 8, 2048, 8320, 4, 128, FAKE, FAKE, FAKE, None, None) == 2  # H % 256
     assert LQ(FAKE, FAKE, 1, 4, 8, 2048, 8192, 4, 256, FAKE, FAKE, FAKE, None, None) == 2  # group
     assert LQ(FAKE, FAKE, 1, 4, 8, 0, 8192, 4, 128, FAKE, FAKE, FAKE, None, None) == 2     # K = 0

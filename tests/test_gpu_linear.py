@@ -76,7 +76,9 @@ def _run(a, w, dtype, bits, group, want_y=True):
 
 
 EXACT = [  # (R, T, K, H, group, bits, dtype)
-    (1, 256, 64, 256, 128, 4, oracle.BF16),     # one tile, one stage
+    (1, 256, 32, 256, 128, 4, oracle.BF16),     # one tile, a single k stage
+    (2, 100, 64, 512, 128, 8, oracle.BF16),     # two k stages
+    (2, 260, 96, 256, 64, 4, oracle.F16),       # three k stages, ragged tokens
     (2, 300, 128, 512, 64, 8, oracle.F16),      # ragged tokens
     (4, 37, 192, 1024, 32, 4, oracle.BF16),     # fewer tokens than a tile, 3 stages
     (4, 520, 256, 768, 8, 8, oracle.BF16),      # group 8; 36 tiles (no XCD regrouping)
