@@ -209,33 +209,37 @@ void linear_quantize_kernel(
         w_off[j] = row * rowb + lchunk * 16u;
         a_off[j] = (row < last_t ? row : last_t) * rowb + lchunk * 16u;
     }
-    auto stage_in = [&](int kt) {
+    // the two loads (W and A rows wrow0 + 16 j ..) of part j of stage kt
+    auto stage_in_part = [&](int kt, int j) {
         const uint32_t kb = (uint32_t)kt * (kTileK * 2);
         uint16_t *sw = lds + (kt % kStages) * kStage;
         uint16_t *sa = sw + kTileN * kTileK;
+        const uint32_t lrow0 = (wrow0 + 16u * j) * kTileK;   // wave-uniform
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void *)(Wc + w_off[j] + kb),
+            (__attribute__((address_space(3))) void *)(sw + lrow0), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void *)(Ac + a_off[j] + kb),
+            (__attribute__((address_space(3))) void *)(sa + lrow0), 16, 0, 0);
+    };
+    auto stage_in = [&](int kt) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t lrow0 = (wrow0 + 16u * j) * kTileK;   // wave-uniform
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(Wc + w_off[j] + kb),
-                (__attribute__((address_space(3))) void *)(sw + lrow0), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(Ac + a_off[j] + kb),
-                (__attribute__((address_space(3))) void *)(sa + lrow0), 16, 0, 0);
-        }
+        for (int j = 0; j < 4; ++j) stage_in_part(kt, j);
     };
 
     // fragment reads: row (block base + lane % 32), chunk 2 ks + lane / 32
     const uint32_t frow = (uint32_t)lane & 31u, fhalf = (uint32_t)lane >> 5;
-    auto frags = [&](int kt, int ks, u32x4 (&fw)[kBlk], u32x4 (&fa)[kBlk]) {
+    // fragments b (W rows and A rows of block b) of step ks of stage kt
+    auto frag_part = [&](int kt, int ks, int b, u32x4 (&fw)[kBlk], u32x4 (&fa)[kBlk]) {
         const uint16_t *sw = lds + (kt % kStages) * kStage;
         const uint16_t *sa = sw + kTileN * kTileK;
         const uint32_t c = 2u * ks + fhalf;
+        fw[b] = *reinterpret_cast<const u32x4 *>(sw + lds_at(wn * kWaveSpan + b * 32 + frow, c));
+        fa[b] = *reinterpret_cast<const u32x4 *>(sa + lds_at(wt * kWaveSpan + b * 32 + frow, c));
+    };
+    auto frags = [&](int kt, int ks, u32x4 (&fw)[kBlk], u32x4 (&fa)[kBlk]) {
 #pragma unroll
-        for (int b = 0; b < kBlk; ++b) {
-            fw[b] = *reinterpret_cast<const u32x4 *>(sw + lds_at(wn * kWaveSpan + b * 32 + frow, c));
-            fa[b] = *reinterpret_cast<const u32x4 *>(sa + lds_at(wt * kWaveSpan + b * 32 + frow, c));
-        }
+        for (int b = 0; b < kBlk; ++b) frag_part(kt, ks, b, fw, fa);
     };
 
     f32x16 acc[kBlk][kBlk];
@@ -253,23 +257,18 @@ void linear_quantize_kernel(
     // first fragments. Every read of a buffer happens before the barrier that
     // precedes its refill.
     u32x4 fw[2][kBlk], fa[2][kBlk];
-    auto step = [&](int ks) {
+    // A step in four chunks: chunk nb = the 4 MFMAs of W block nb, then
+    // `side(nb)` (the LDS reads and staging loads that overlap them); nothing
+    // moves across chunks, so the loads are spread between the MFMAs.
+    auto step = [&](int ks, auto &&side) {
 #pragma unroll
-        for (int nb = 0; nb < kBlk; ++nb)
+        for (int nb = 0; nb < kBlk; ++nb) {
 #pragma unroll
             for (int tb = 0; tb < kBlk; ++tb)
                 acc[nb][tb] = mfma<DT>(fw[ks & 1][nb], fa[ks & 1][tb], acc[nb][tb]);
-    };
-    // 16 MFMAs interleaved with 8 LDS reads and optionally the 8 staging loads
-    auto interleave = [&](bool lds_reads, bool vmem) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (vmem) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            if (lds_reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            side(nb);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
     };
     // ISSUE: stage kt + kStages - 1 exists; PEND: stages issued after kt + 1
     // (0, 1 or 2 -- they may stay in flight); LAST: no stage follows
@@ -277,17 +276,17 @@ void linear_quantize_kernel(
         constexpr bool ISSUE = decltype(issue_tag)::value;
         constexpr int PEND = decltype(pend_tag)::value;
         constexpr bool LAST = decltype(last_tag)::value;
-        if constexpr (ISSUE) stage_in(kt + kStages - 1);
-        frags(kt, 1, fw[1], fa[1]);
-        step(0);
-        interleave(true, ISSUE);
+        step(0, [&](int nb) {
+            if constexpr (ISSUE) stage_in_part(kt + kStages - 1, nb);
+            frag_part(kt, 1, nb, fw[1], fa[1]);
+        });
         if constexpr (!LAST) {
             wait_loads<PEND * kLoadsPerStage>();
             barrier_keep_loads();
-            frags(kt + 1, 0, fw[0], fa[0]);
+            step(1, [&](int nb) { frag_part(kt + 1, 0, nb, fw[0], fa[0]); });
+        } else {
+            step(1, [&](int) {});
         }
-        step(1);
-        interleave(!LAST, false);
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
