@@ -53,6 +53,9 @@ constexpr int kBlk = kWaveSpan / 32;        // 32 x 32 MFMA blocks per wave side
 constexpr int kStage = (kTileN + kTileT) * kTileK;   // 16-bit elements per stage
 constexpr int kGroupT = 4;                  // token tiles per scheduling group
 constexpr int kXcds = 8;
+// buffer resource word 3 for raw (untyped, unswizzled) 32-bit-addressed
+// buffers on gfx9-family GPUs
+constexpr int kRawBufferFlags = 0x00020000;
 
 static_assert(kBlockThreads == 256, "four waves per workgroup");
 
@@ -187,40 +190,38 @@ void linear_quantize_kernel(
     const uint16_t *Wb = W + ((size_t)r * H + n0) * (size_t)K;
     const uint16_t *Ab = A + ((size_t)r * T + t0) * (size_t)K;
     const uint32_t rowb = (uint32_t)K * 2u;          // bytes per operand row
-    const uint32_t last_t = (uint32_t)(T - 1 - t0);  // rows past it re-read it (ragged T)
 
-    // Staging, global -> LDS directly (global_load_lds_dwordx4: lane i's 16
-    // bytes land at the instruction's LDS base + 16 i). One instruction fills
-    // 16 staged rows of 64 bytes; lane i serves row i / 4 at chunk position
-    // i % 4, so it fetches the operand's chunk (i % 4) ^ ((row / 4) % 4) --
-    // the rotation lds_at reads back. Wave w fills rows w*64 .. w*64+63 of
-    // both tiles (4 instructions each, 8 per stage). Token rows past the end
-    // re-read the last one.
+    // Staging, global -> LDS directly (buffer_load_dwordx4 ... lds: lane i's
+    // 16 bytes land at the instruction's LDS base + 16 i). One instruction
+    // fills 16 staged rows of 64 bytes; lane i serves row i / 4 at chunk
+    // position i % 4, so it fetches the operand's chunk (i % 4) ^ ((row / 4) %
+    // 4) -- the rotation lds_at reads back. Wave w fills rows w*64 .. w*64+63
+    // of both tiles (4 instructions each, 8 per stage). Addresses are a
+    // buffer resource per operand tile (SGPRs), a fixed 32-bit lane offset and
+    // the stage's k offset as the scalar offset. The A resource covers only
+    // the tile's real token rows: rows past T read as zeros (their outputs are
+    // never stored).
     constexpr int kLoadsPerStage = 8;            // per wave
     const uint32_t lrow = (uint32_t)lane >> 2;   // row within the instruction's 16
     const uint32_t lchunk = ((uint32_t)lane & 3u) ^ ((lrow >> 2) & 3u);
     const uint32_t wrow0 = (uint32_t)wave * 64u;
-    const char *Wc = reinterpret_cast<const char *>(Wb);
-    const char *Ac = reinterpret_cast<const char *>(Ab);
-    uint32_t w_off[4], a_off[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t row = wrow0 + 16u * j + lrow;
-        w_off[j] = row * rowb + lchunk * 16u;
-        a_off[j] = (row < last_t ? row : last_t) * rowb + lchunk * 16u;
-    }
+    const int t_rows = min(kTileT, T - t0);
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(Wb), (short)0, (int)(kTileN * rowb), kRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(Ab), (short)0, (int)((uint32_t)t_rows * rowb), kRawBufferFlags);
+    const uint32_t voff = (wrow0 + lrow) * rowb + lchunk * 16u;   // + 16 j rows
     // the two loads (W and A rows wrow0 + 16 j ..) of part j of stage kt
     auto stage_in_part = [&](int kt, int j) {
-        const uint32_t kb = (uint32_t)kt * (kTileK * 2);
+        const int kb = kt * (kTileK * 2);
         uint16_t *sw = lds + (kt % kStages) * kStage;
         uint16_t *sa = sw + kTileN * kTileK;
         const uint32_t lrow0 = (wrow0 + 16u * j) * kTileK;   // wave-uniform
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void *)(Wc + w_off[j] + kb),
-            (__attribute__((address_space(3))) void *)(sw + lrow0), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void *)(Ac + a_off[j] + kb),
-            (__attribute__((address_space(3))) void *)(sa + lrow0), 16, 0, 0);
+        const uint32_t vo = voff + 16u * j * rowb;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wres, (__attribute__((address_space(3))) void *)(sw + lrow0), 16, vo, kb, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ares, (__attribute__((address_space(3))) void *)(sa + lrow0), 16, vo, kb, 0, 0);
     };
     auto stage_in = [&](int kt) {
 #pragma unroll

@@ -77,10 +77,12 @@ def _run(a, w, dtype, bits, group, want_y=True):
 
 EXACT = [  # (R, T, K, H, group, bits, dtype)
     (1, 256, 32, 256, 128, 4, oracle.BF16),     # one tile, a single k stage
-    (2, 100, 64, 512, 128, 8, oracle.BF16),     # two k stages
-    (2, 260, 96, 256, 64, 4, oracle.F16),       # three k stages, ragged tokens
+    (1, 256, 64, 256, 128, 4, oracle.BF16),     # two stages
+    (2, 260, 96, 256, 64, 4, oracle.F16),       # three stages, ragged tokens
+    (2, 100, 128, 512, 128, 8, oracle.BF16),    # four stages: the ring turns over once
+    (2, 260, 320, 256, 64, 4, oracle.F16),      # ten stages
     (2, 300, 128, 512, 64, 8, oracle.F16),      # ragged tokens
-    (4, 37, 192, 1024, 32, 4, oracle.BF16),     # fewer tokens than a tile, 3 stages
+    (4, 37, 192, 1024, 32, 4, oracle.BF16),     # fewer tokens than a tile, 6 stages
     (4, 520, 256, 768, 8, 8, oracle.BF16),      # group 8; 36 tiles (no XCD regrouping)
     (3, 256, 64, 768, 16, 4, oracle.F16),       # R = 3
     (4, 512, 2048, 8192, 128, 4, oracle.BF16),  # LLaMA-3-70B o_proj per rank, 512 tokens
