@@ -73,21 +73,15 @@ __global__ __launch_bounds__(kBlockThreads) void dsr_kernel(
             zv[u] = zb[mrel[u]];
         }
     };
-    // x_hat = fp32(q*s + z): q*s is exact (<= 8 x 11 significant bits), so
-    // the fused multiply-add rounds exactly once, as the method does.
+    // x_hat = fp32(q*s + z), rounded once (dequant8)
     auto add_operand = [&](bool first, const uint32_t (&w)[U][W], const uint16_t (&sv)[U],
                            const uint16_t (&zv)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float q[kLaneElems];
-            decode8<BITS1>(w[u], q);
-            const float s = half_bits_to_float(sv[u]);
-            const float z = half_bits_to_float(zv[u]);
+            float xh[kLaneElems];
+            dequant8<BITS1>(w[u], sv[u], zv[u], xh);
 #pragma unroll
-            for (int k = 0; k < kLaneElems; ++k) {
-                const float xh = __builtin_fmaf(q[k], s, z);
-                y[u][k] = first ? xh : y[u][k] + xh;
-            }
+            for (int k = 0; k < kLaneElems; ++k) y[u][k] = first ? xh[k] : y[u][k] + xh[k];
         }
     };
 

@@ -277,6 +277,51 @@ __device__ __forceinline__ void decode8(const uint32_t (&w)[BITS == 4 ? 1 : 2], 
     }
 }
 
+// Dequantized values x_k = fp32(q_k * s + z) of 8 codes, for a scale s and
+// zero z given as fp16 bit patterns. The codes are spread into the 16-bit
+// halves of four registers (one mask, or a shift and a mask, per register);
+// read as fp16, a half holding the integer q is the subnormal q * 2^-24,
+// exactly. One mixed-precision fma per value (v_fma_mix_f32: the fp16 half
+// selected in place, the binary32 scale s * 2^24, the fp16 zero) then forms
+// (q * 2^-24) * (s * 2^24) + z: the product is the exact q*s (at most 8 x 11
+// significant bits) and the sum is rounded once, exactly as fp32(q*s + z).
+// This needs fp16 subnormals preserved on input (they are: the build keeps
+// the default denormal mode, checked by the instruction guard test).
+template <int BITS>
+__device__ __forceinline__ void dequant8(const uint32_t (&w)[BITS == 4 ? 1 : 2], uint16_t s16,
+                                         uint16_t z16, float (&x)[kLaneElems]) {
+    uint32_t p[4];
+    int e_lo[4], e_hi[4];   // elements held in the low and high halves of p[i]
+    if constexpr (BITS == 4) {
+        // byte i = q(2i) | q(2i+1) << 4: bits 4k of each 16-bit half are elements k, 4 + k
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            p[k] = (w[0] >> (4 * k)) & 0x000F000Fu;
+            e_lo[k] = k;
+            e_hi[k] = 4 + k;
+        }
+    } else {
+        // word j holds elements 4j..4j+3, one per byte
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            p[2 * j] = w[j] & 0x00FF00FFu;
+            p[2 * j + 1] = (w[j] >> 8) & 0x00FF00FFu;
+            e_lo[2 * j] = 4 * j;
+            e_hi[2 * j] = 4 * j + 2;
+            e_lo[2 * j + 1] = 4 * j + 1;
+            e_hi[2 * j + 1] = 4 * j + 3;
+        }
+    }
+    const float sc = (float)__builtin_bit_cast(_Float16, s16) * 16777216.0f;   // s * 2^24, exact
+    const float z = (float)__builtin_bit_cast(_Float16, z16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const f16x2 h = __builtin_bit_cast(f16x2, p[k]);
+        x[e_lo[k]] = __builtin_fmaf((float)h.x, sc, z);
+        x[e_hi[k]] = __builtin_fmaf((float)h.y, sc, z);
+    }
+}
+
 // Quantize a tile of U slots: v holds the lane's 8 values per slot, mn/mx
 // their in-lane minima and maxima. Each group's min/max is reduced over its
 // S slots and L lanes, its scale/zero/reciprocal computed, and the codes
