@@ -29,9 +29,10 @@
 //     (global_load_lds), three stages ahead of the matrix cores; each 64-byte
 //     row's four 16-byte chunks are rotated by (row / 4) % 4 so that the
 //     fragment reads (32 rows x one chunk) are free of bank conflicts;
-//   - workgroups are numbered so that each XCD (its own L2) runs a contiguous
-//     run of tiles, ordered 4 token tiles x all channel tiles, so that
-//     concurrently running workgroups share their A and W stage tiles in L2.
+//   - one persistent workgroup per CU walks its tiles; each XCD (its own L2)
+//     runs a contiguous run of tiles, ordered 4 token tiles x all channel
+//     tiles, so that concurrently running workgroups share their A and W
+//     stage tiles in L2, and a tile's stores drain during the next tile.
 #include <type_traits>
 
 #include "fc_device.h"
@@ -162,8 +163,8 @@ template <int DT, int BITS, int G>
 __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void linear_quantize_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int T, int K, int H,
-    int tiles_t, int tiles_n, int total, uint8_t *__restrict__ codes, uint16_t *__restrict__ s,
-    uint16_t *__restrict__ z, uint16_t *__restrict__ y) {
+    int tiles_t, int tiles_n, int total, int grid, uint8_t *__restrict__ codes,
+    uint16_t *__restrict__ s, uint16_t *__restrict__ z, uint16_t *__restrict__ y) {
     static_assert(G >= 8 && G <= kWaveSpan && (G & (G - 1)) == 0, "group of 8..128 channels");
     __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * kStage];
 
@@ -172,246 +173,277 @@ void linear_quantize_kernel(
     const int wave = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
     const int wn = wave & 1, wt = wave >> 1;
 
-    // workgroup -> tile: XCD-contiguous runs, then kGroupT token tiles x all
-    // channel tiles of one rank
+    // Persistent workgroups (`grid` of them, one per CU). Tile order: each XCD (its own L2)
+    // runs a contiguous run of tiles -- workgroup b runs on XCD b % 8 and
+    // takes every (grid/8)-th tile of its XCD's run -- and within a run
+    // kGroupT token tiles x all channel tiles of one rank. A workgroup's
+    // stores of one tile drain while it computes the next.
     const int bid = (int)__builtin_amdgcn_workgroup_id_x();
-    const int logical = (total % kXcds == 0) ? (bid % kXcds) * (total / kXcds) + bid / kXcds : bid;
-    const int per_rank = tiles_t * tiles_n;
-    const int r = logical / per_rank;
-    const int i = logical - r * per_rank;
-    const int grp = i / (kGroupT * tiles_n);
-    const int first_t = grp * kGroupT;
-    const int gsize = min(tiles_t - first_t, kGroupT);
-    const int in_grp = i - grp * kGroupT * tiles_n;
-    const int tile_t = first_t + in_grp % gsize;
-    const int tile_n = in_grp / gsize;
-    const int n0 = tile_n * kTileN, t0 = tile_t * kTileT;
-
-    const uint16_t *Wb = W + ((size_t)r * H + n0) * (size_t)K;
-    const uint16_t *Ab = A + ((size_t)r * T + t0) * (size_t)K;
-    const uint32_t rowb = (uint32_t)K * 2u;          // bytes per operand row
-
-    // Staging, global -> LDS directly (buffer_load_dwordx4 ... lds: lane i's
-    // 16 bytes land at the instruction's LDS base + 16 i). One instruction
-    // fills 16 staged rows of 64 bytes; lane i serves row i / 4 at chunk
-    // position i % 4, so it fetches the operand's chunk (i % 4) ^ ((row / 4) %
-    // 4) -- the rotation lds_at reads back. Wave w fills rows w*64 .. w*64+63
-    // of both tiles (4 instructions each, 8 per stage). Addresses are a
-    // buffer resource per operand tile (SGPRs), a fixed 32-bit lane offset and
-    // the stage's k offset as the scalar offset. The A resource covers only
-    // the tile's real token rows: rows past T read as zeros (their outputs are
-    // never stored).
-    constexpr int kLoadsPerStage = 8;            // per wave
-    const uint32_t lrow = (uint32_t)lane >> 2;   // row within the instruction's 16
-    const uint32_t lchunk = ((uint32_t)lane & 3u) ^ ((lrow >> 2) & 3u);
-    const uint32_t wrow0 = (uint32_t)wave * 64u;
-    const int t_rows = min(kTileT, T - t0);
-    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(Wb), (short)0, (int)(kTileN * rowb), kRawBufferFlags);
-    const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(Ab), (short)0, (int)((uint32_t)t_rows * rowb), kRawBufferFlags);
-    const uint32_t voff = (wrow0 + lrow) * rowb + lchunk * 16u;   // + 16 j rows
-    // the two loads (W and A rows wrow0 + 16 j ..) of part j of stage kt
-    auto stage_in_part = [&](int kt, int j) {
-        const int kb = kt * (kTileK * 2);
-        uint16_t *sw = lds + (kt % kStages) * kStage;
-        uint16_t *sa = sw + kTileN * kTileK;
-        const uint32_t lrow0 = (wrow0 + 16u * j) * kTileK;   // wave-uniform
-        const uint32_t vo = voff + 16u * j * rowb;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            wres, (__attribute__((address_space(3))) void *)(sw + lrow0), 16, vo, kb, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ares, (__attribute__((address_space(3))) void *)(sa + lrow0), 16, vo, kb, 0, 0);
-    };
-    auto stage_in = [&](int kt) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) stage_in_part(kt, j);
-    };
-
-    // fragment reads: row (block base + lane % 32), chunk 2 ks + lane / 32
-    const uint32_t frow = (uint32_t)lane & 31u, fhalf = (uint32_t)lane >> 5;
-    // fragments b (W rows and A rows of block b) of step ks of stage kt
-    auto frag_part = [&](int kt, int ks, int b, u32x4 (&fw)[kBlk], u32x4 (&fa)[kBlk]) {
-        const uint16_t *sw = lds + (kt % kStages) * kStage;
-        const uint16_t *sa = sw + kTileN * kTileK;
-        const uint32_t c = 2u * ks + fhalf;
-        fw[b] = *reinterpret_cast<const u32x4 *>(sw + lds_at(wn * kWaveSpan + b * 32 + frow, c));
-        fa[b] = *reinterpret_cast<const u32x4 *>(sa + lds_at(wt * kWaveSpan + b * 32 + frow, c));
-    };
-    auto frags = [&](int kt, int ks, u32x4 (&fw)[kBlk], u32x4 (&fa)[kBlk]) {
-#pragma unroll
-        for (int b = 0; b < kBlk; ++b) frag_part(kt, ks, b, fw, fa);
-    };
-
-    f32x16 acc[kBlk][kBlk];
-#pragma unroll
-    for (int a = 0; a < kBlk; ++a)
-#pragma unroll
-        for (int b = 0; b < kBlk; ++b) acc[a][b] = f32x16{};
-
-    // One stage = 2 steps of k = 16, 16 MFMAs each, over an LDS ring of
-    // kStages buffers. At stage kt the loads of stage kt + kStages - 1 go out
-    // (into the buffer stage kt - 1 used); step 0's MFMAs overlap the reads of
-    // step 1's fragments; then this wave waits until its loads of stage kt + 1
-    // have landed (the later stages' loads stay in flight) and the workgroup
-    // barrier publishes stage kt + 1; step 1's MFMAs overlap the reads of its
-    // first fragments. Every read of a buffer happens before the barrier that
-    // precedes its refill.
-    u32x4 fw[2][kBlk], fa[2][kBlk];
-    // A step in four chunks: chunk nb = the 4 MFMAs of W block nb, then
-    // `side(nb)` (the LDS reads and staging loads that overlap them); nothing
-    // moves across chunks, so the loads are spread between the MFMAs.
-    auto step = [&](int ks, auto &&side) {
-#pragma unroll
-        for (int nb = 0; nb < kBlk; ++nb) {
-#pragma unroll
-            for (int tb = 0; tb < kBlk; ++tb)
-                acc[nb][tb] = mfma<DT>(fw[ks & 1][nb], fa[ks & 1][tb], acc[nb][tb]);
-            side(nb);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    // ISSUE: stage kt + kStages - 1 exists; PEND: stages issued after kt + 1
-    // (0, 1 or 2 -- they may stay in flight); LAST: no stage follows
-    auto stage = [&](int kt, auto issue_tag, auto pend_tag, auto last_tag) {
-        constexpr bool ISSUE = decltype(issue_tag)::value;
-        constexpr int PEND = decltype(pend_tag)::value;
-        constexpr bool LAST = decltype(last_tag)::value;
-        step(0, [&](int nb) {
-            if constexpr (ISSUE) stage_in_part(kt + kStages - 1, nb);
-            frag_part(kt, 1, nb, fw[1], fa[1]);
-        });
-        if constexpr (!LAST) {
-            wait_loads<PEND * kLoadsPerStage>();
-            barrier_keep_loads();
-            step(1, [&](int nb) { frag_part(kt + 1, 0, nb, fw[0], fa[0]); });
+    const bool by_xcd = total % kXcds == 0 && grid % kXcds == 0;
+    for (int it = 0;; ++it) {
+        int logical;
+        if (by_xcd) {
+            const int slot = it * (grid / kXcds) + bid / kXcds;
+            if (slot >= total / kXcds) break;
+            logical = (bid % kXcds) * (total / kXcds) + slot;
         } else {
-            step(1, [&](int) {});
+            logical = it * grid + bid;
+            if (logical >= total) break;
         }
-    };
-    using T_ = std::true_type;
-    using F_ = std::false_type;
-    using P0 = std::integral_constant<int, 0>;
-    using P1 = std::integral_constant<int, 1>;
-    using P2 = std::integral_constant<int, 2>;
+        const int per_rank = tiles_t * tiles_n;
+        const int r = logical / per_rank;
+        const int i = logical - r * per_rank;
+        const int grp = i / (kGroupT * tiles_n);
+        const int first_t = grp * kGroupT;
+        const int gsize = min(tiles_t - first_t, kGroupT);
+        const int in_grp = i - grp * kGroupT * tiles_n;
+        const int tile_t = first_t + in_grp % gsize;
+        const int tile_n = in_grp / gsize;
+        const int n0 = tile_n * kTileN, t0 = tile_t * kTileT;
 
-    const int KT = K / kTileK;
-    // prologue: the first min(KT, kStages - 1) stages; wait for stage 0
-    stage_in(0);
-    if (KT > 1) stage_in(1);
-    if (KT > 2) stage_in(2);
-    if (KT > 2) wait_loads<2 * kLoadsPerStage>();
-    else if (KT > 1) wait_loads<kLoadsPerStage>();
-    else wait_loads<0>();
-    barrier_keep_loads();
-    frags(0, 0, fw[0], fa[0]);
-    for (int kt = 0; kt + 3 < KT; ++kt) stage(kt, T_{}, P2{}, F_{});
-    if (KT >= 3) stage(KT - 3, F_{}, P1{}, F_{});
-    if (KT >= 2) stage(KT - 2, F_{}, P0{}, F_{});
-    stage(KT - 1, F_{}, P0{}, T_{});
+        const uint16_t *Wb = W + ((size_t)r * H + n0) * (size_t)K;
+        const uint16_t *Ab = A + ((size_t)r * T + t0) * (size_t)K;
+        const uint32_t rowb = (uint32_t)K * 2u;          // bytes per operand row
 
-    // ---- epilogue: round to the dtype, quantize per (token, group) ----
-    // Run j = 4 nb + m of a lane holds channels nb*32 + 8m + 4*(lane/32) + 0..3
-    // of the wave's span (accumulator entries 4m..4m+3 of block nb); a group
-    // of G channels is RG = G/8 consecutive runs of each lane of the pair.
-    // Codes, scales and zeros of the whole tile are first gathered in LDS (the
-    // operand buffers are free by then) and then written out row by row in
-    // 16-byte pieces: a token row of the tile is one contiguous run of codes.
-    constexpr int RG = G / 8;
-    constexpr int kCodeRow = kTileN * BITS / 8;      // code bytes of a tile row
-    constexpr int kCodePitch = kCodeRow + 16;        // padded (spreads LDS banks)
-    constexpr int kMetaRow = kTileN / G * 2;         // bytes of s (or z) of a tile row
-    static_assert(kTileT * (kCodePitch + 2 * kMetaRow) <= kStages * kStage * 2, "tile fits in LDS");
-    uint8_t *lc = reinterpret_cast<uint8_t *>(lds);
-    uint8_t *lsz = lc + kTileT * kCodePitch;         // s rows, then z rows
-    const int Hg = H / G;
-    const uint32_t h4 = 4u * fhalf;
-    const uint32_t lane_y = frow * (uint32_t)H * 2u;
-    __syncthreads();   // every wave has read its last operand fragments
-#pragma unroll
-    for (int tb = 0; tb < kBlk; ++tb) {
-        const uint32_t tl = (uint32_t)(wt * kWaveSpan + tb * 32) + frow;   // token in the tile
-        const int trow0 = t0 + wt * kWaveSpan + tb * 32;
-        const bool live = trow0 + (int)frow < T;
-        uint16_t *yb = y ? y + ((size_t)r * T + (size_t)trow0) * (size_t)H +
-                               (size_t)(n0 + wn * kWaveSpan)
-                         : nullptr;
-#pragma unroll
-        for (int gi = 0; gi < kWaveSpan / G; ++gi) {
-            // the group's values rounded to the dtype: packed pairs (yw) and
-            // widened back to binary32 (yv) -- what the layer would store
-            float yv[RG][4];
-            uint32_t yw[RG][2];
-#pragma unroll
-            for (int jj = 0; jj < RG; ++jj) {
-                const int j = gi * RG + jj;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    yw[jj][h] = pack2<DT>(acc[j / 4][tb][(j % 4) * 4 + 2 * h],
-                                          acc[j / 4][tb][(j % 4) * 4 + 2 * h + 1]);
-                    unpack2<DT>(yw[jj][h], yv[jj][2 * h], yv[jj][2 * h + 1]);
+        // Staging, global -> LDS directly (buffer_load_dwordx4 ... lds: lane i's
+        // 16 bytes land at the instruction's LDS base + 16 i). One instruction
+        // fills 16 staged rows of 64 bytes; lane i serves row i / 4 at chunk
+        // position i % 4, so it fetches the operand's chunk (i % 4) ^ ((row / 4) %
+        // 4) -- the rotation lds_at reads back. Wave w fills rows w*64 .. w*64+63
+        // of both tiles (4 instructions each, 8 per stage). Addresses are a
+        // buffer resource per operand tile (SGPRs), a fixed 32-bit lane offset and
+        // the stage's k offset as the scalar offset. The A resource covers only
+        // the tile's real token rows: rows past T read as zeros (their outputs are
+        // never stored).
+        constexpr int kLoadsPerStage = 8;            // per wave
+        const uint32_t lrow = (uint32_t)lane >> 2;   // row within the instruction's 16
+        const uint32_t lchunk = ((uint32_t)lane & 3u) ^ ((lrow >> 2) & 3u);
+        const uint32_t wrow0 = (uint32_t)wave * 64u;
+        const int t_rows = min(kTileT, T - t0);
+        const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(Wb), (short)0, (int)(kTileN * rowb), kRawBufferFlags);
+        const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(Ab), (short)0, (int)((uint32_t)t_rows * rowb), kRawBufferFlags);
+        const uint32_t voff = (wrow0 + lrow) * rowb + lchunk * 16u;   // + 16 j rows
+        // the two loads (W and A rows wrow0 + 16 j ..) of part j of stage kt
+        auto stage_in_part = [&](int kt, int j) {
+            const int kb = kt * (kTileK * 2);
+            uint16_t *sw = lds + (kt % kStages) * kStage;
+            uint16_t *sa = sw + kTileN * kTileK;
+            const uint32_t lrow0 = (wrow0 + 16u * j) * kTileK;   // wave-uniform
+            const uint32_t vo = voff + 16u * j * rowb;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wres, (__attribute__((address_space(3))) void *)(sw + lrow0), 16, vo, kb, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ares, (__attribute__((address_space(3))) void *)(sa + lrow0), 16, vo, kb, 0, 0);
+        };
+        auto stage_in = [&](int kt) {
+    #pragma unroll
+            for (int j = 0; j < 4; ++j) stage_in_part(kt, j);
+        };
+
+        // fragment reads: row (block base + lane % 32), chunk 2 ks + lane / 32
+        const uint32_t frow = (uint32_t)lane & 31u, fhalf = (uint32_t)lane >> 5;
+        // fragments b (W rows and A rows of block b) of step ks of stage kt
+        auto frag_part = [&](int kt, int ks, int b, u32x4 (&fw)[kBlk], u32x4 (&fa)[kBlk]) {
+            const uint16_t *sw = lds + (kt % kStages) * kStage;
+            const uint16_t *sa = sw + kTileN * kTileK;
+            const uint32_t c = 2u * ks + fhalf;
+            fw[b] = *reinterpret_cast<const u32x4 *>(sw + lds_at(wn * kWaveSpan + b * 32 + frow, c));
+            fa[b] = *reinterpret_cast<const u32x4 *>(sa + lds_at(wt * kWaveSpan + b * 32 + frow, c));
+        };
+        auto frags = [&](int kt, int ks, u32x4 (&fw)[kBlk], u32x4 (&fa)[kBlk]) {
+    #pragma unroll
+            for (int b = 0; b < kBlk; ++b) frag_part(kt, ks, b, fw, fa);
+        };
+
+        f32x16 acc[kBlk][kBlk];
+    #pragma unroll
+        for (int a = 0; a < kBlk; ++a)
+    #pragma unroll
+            for (int b = 0; b < kBlk; ++b) acc[a][b] = f32x16{};
+
+        // One stage = 2 steps of k = 16, 16 MFMAs each, over an LDS ring of
+        // kStages buffers. At stage kt the loads of stage kt + kStages - 1 go out
+        // (into the buffer stage kt - 1 used); step 0's MFMAs overlap the reads of
+        // step 1's fragments; then this wave waits until its loads of stage kt + 1
+        // have landed (the later stages' loads stay in flight) and the workgroup
+        // barrier publishes stage kt + 1; step 1's MFMAs overlap the reads of its
+        // first fragments. Every read of a buffer happens before the barrier that
+        // precedes its refill.
+        u32x4 fw[2][kBlk], fa[2][kBlk];
+        // A step in four chunks: chunk nb = the 4 MFMAs of W block nb, then
+        // `side(nb)` (the LDS reads and staging loads that overlap them); nothing
+        // moves across chunks, so the loads are spread between the MFMAs.
+        auto step = [&](int ks, auto &&side) {
+    #pragma unroll
+            for (int nb = 0; nb < kBlk; ++nb) {
+    #pragma unroll
+                for (int tb = 0; tb < kBlk; ++tb)
+                    acc[nb][tb] = mfma<DT>(fw[ks & 1][nb], fa[ks & 1][tb], acc[nb][tb]);
+                side(nb);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // ISSUE: stage kt + kStages - 1 exists; PEND: stages issued after kt + 1
+        // (0, 1 or 2 -- they may stay in flight); LAST: no stage follows
+        auto stage = [&](int kt, auto issue_tag, auto pend_tag, auto last_tag) {
+            constexpr bool ISSUE = decltype(issue_tag)::value;
+            constexpr int PEND = decltype(pend_tag)::value;
+            constexpr bool LAST = decltype(last_tag)::value;
+            step(0, [&](int nb) {
+                if constexpr (ISSUE) stage_in_part(kt + kStages - 1, nb);
+                frag_part(kt, 1, nb, fw[1], fa[1]);
+            });
+            if constexpr (!LAST) {
+                wait_loads<PEND * kLoadsPerStage>();
+                barrier_keep_loads();
+                step(1, [&](int nb) { frag_part(kt + 1, 0, nb, fw[0], fa[0]); });
+            } else {
+                step(1, [&](int) {});
+            }
+        };
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
+        using P2 = std::integral_constant<int, 2>;
+
+        const int KT = K / kTileK;
+        // prologue: the first min(KT, kStages - 1) stages; wait for stage 0
+        stage_in(0);
+        if (KT > 1) stage_in(1);
+        if (KT > 2) stage_in(2);
+        if (KT > 2) wait_loads<2 * kLoadsPerStage>();
+        else if (KT > 1) wait_loads<kLoadsPerStage>();
+        else wait_loads<0>();
+        barrier_keep_loads();
+        frags(0, 0, fw[0], fa[0]);
+        for (int kt = 0; kt + 3 < KT; ++kt) stage(kt, T_{}, P2{}, F_{});
+        if (KT >= 3) stage(KT - 3, F_{}, P1{}, F_{});
+        if (KT >= 2) stage(KT - 2, F_{}, P0{}, F_{});
+        stage(KT - 1, F_{}, P0{}, T_{});
+
+        // ---- epilogue: round to the dtype, quantize per (token, group) ----
+        // Run j = 4 nb + m of a lane holds channels nb*32 + 8m + 4*(lane/32) + 0..3
+        // of the wave's span (accumulator entries 4m..4m+3 of block nb); a group
+        // of G channels is RG = G/8 consecutive runs of each lane of the pair.
+        // Codes, scales and zeros of the whole tile are first gathered in LDS (the
+        // operand buffers are free by then) and then written out row by row in
+        // 16-byte pieces: a token row of the tile is one contiguous run of codes.
+        constexpr int RG = G / 8;
+        constexpr int kCodeRow = kTileN * BITS / 8;      // code bytes of a tile row
+        constexpr int kCodePitch = kCodeRow + 16;        // padded (spreads LDS banks)
+        constexpr int kMetaRow = kTileN / G * 2;         // bytes of s (or z) of a tile row
+        static_assert(kTileT * (kCodePitch + 2 * kMetaRow) <= kStages * kStage * 2, "tile fits in LDS");
+        uint8_t *lc = reinterpret_cast<uint8_t *>(lds);
+        uint8_t *lsz = lc + kTileT * kCodePitch;         // s rows, then z rows
+        const int Hg = H / G;
+        const uint32_t h4 = 4u * fhalf;
+        const uint32_t lane_y = frow * (uint32_t)H * 2u;
+        __syncthreads();   // every wave has read its last operand fragments
+    #pragma unroll
+        for (int tb = 0; tb < kBlk; ++tb) {
+            const uint32_t tl = (uint32_t)(wt * kWaveSpan + tb * 32) + frow;   // token in the tile
+            const int trow0 = t0 + wt * kWaveSpan + tb * 32;
+            const bool live = trow0 + (int)frow < T;
+            uint16_t *yb = y ? y + ((size_t)r * T + (size_t)trow0) * (size_t)H +
+                                   (size_t)(n0 + wn * kWaveSpan)
+                             : nullptr;
+    #pragma unroll
+            for (int gi = 0; gi < kWaveSpan / G; ++gi) {
+                // the group's values rounded to the dtype: packed pairs (yw) and
+                // widened back to binary32 (yv) -- what the layer would store
+                float yv[RG][4];
+                uint32_t yw[RG][2];
+    #pragma unroll
+                for (int jj = 0; jj < RG; ++jj) {
+                    const int j = gi * RG + jj;
+    #pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        yw[jj][h] = pack2<DT>(acc[j / 4][tb][(j % 4) * 4 + 2 * h],
+                                              acc[j / 4][tb][(j % 4) * 4 + 2 * h + 1]);
+                        unpack2<DT>(yw[jj][h], yv[jj][2 * h], yv[jj][2 * h + 1]);
+                    }
+                }
+                float mn = yv[0][0], mx = yv[0][0];
+    #pragma unroll
+                for (int jj = 0; jj < RG; ++jj) {
+                    mn = __builtin_fminf(mn, __builtin_fminf(__builtin_fminf(yv[jj][0], yv[jj][1]),
+                                                             __builtin_fminf(yv[jj][2], yv[jj][3])));
+                    mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(yv[jj][0], yv[jj][1]),
+                                                             __builtin_fmaxf(yv[jj][2], yv[jj][3])));
+                }
+                pair_minmax(mn, mx);
+                const GroupParams p = group_params<BITS>(mn, mx);
+    #pragma unroll
+                for (int jj = 0; jj < RG; ++jj) {
+                    const int j = gi * RG + jj;
+                    const uint32_t ch = (uint32_t)((j / 4) * 32 + (j % 4) * 8) + h4;   // in the wave span
+                    const uint32_t q = encode4<BITS>(yv[jj], p);
+                    const uint32_t at = tl * kCodePitch + (wn * kWaveSpan + ch) * BITS / 8;
+                    if constexpr (BITS == 8)
+                        *reinterpret_cast<uint32_t *>(lc + at) = q;
+                    else
+                        *reinterpret_cast<uint16_t *>(lc + at) = (uint16_t)q;
+                    if (yb && live) stv<u32x2, false>(yb, lane_y + ch * 2u, u32x2{yw[jj][0], yw[jj][1]});
+                }
+                if (fhalf == 0) {
+                    const uint32_t m = tl * kMetaRow + (uint32_t)(wn * (kWaveSpan / G) + gi) * 2u;
+                    *reinterpret_cast<uint16_t *>(lsz + m) = p.s16;
+                    *reinterpret_cast<uint16_t *>(lsz + kTileT * kMetaRow + m) = p.z16;
                 }
             }
-            float mn = yv[0][0], mx = yv[0][0];
-#pragma unroll
-            for (int jj = 0; jj < RG; ++jj) {
-                mn = __builtin_fminf(mn, __builtin_fminf(__builtin_fminf(yv[jj][0], yv[jj][1]),
-                                                         __builtin_fminf(yv[jj][2], yv[jj][3])));
-                mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(yv[jj][0], yv[jj][1]),
-                                                         __builtin_fmaxf(yv[jj][2], yv[jj][3])));
-            }
-            pair_minmax(mn, mx);
-            const GroupParams p = group_params<BITS>(mn, mx);
-#pragma unroll
-            for (int jj = 0; jj < RG; ++jj) {
-                const int j = gi * RG + jj;
-                const uint32_t ch = (uint32_t)((j / 4) * 32 + (j % 4) * 8) + h4;   // in the wave span
-                const uint32_t q = encode4<BITS>(yv[jj], p);
-                const uint32_t at = tl * kCodePitch + (wn * kWaveSpan + ch) * BITS / 8;
-                if constexpr (BITS == 8)
-                    *reinterpret_cast<uint32_t *>(lc + at) = q;
-                else
-                    *reinterpret_cast<uint16_t *>(lc + at) = (uint16_t)q;
-                if (yb && live) stv<u32x2, false>(yb, lane_y + ch * 2u, u32x2{yw[jj][0], yw[jj][1]});
-            }
-            if (fhalf == 0) {
-                const uint32_t m = tl * kMetaRow + (uint32_t)(wn * (kWaveSpan / G) + gi) * 2u;
-                *reinterpret_cast<uint16_t *>(lsz + m) = p.s16;
-                *reinterpret_cast<uint16_t *>(lsz + kTileT * kMetaRow + m) = p.z16;
-            }
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // write-out of the tile's live token rows
-    const int rows = min(kTileT, T - t0);
-    const size_t grow0 = (size_t)r * T + (size_t)t0;
-    uint8_t *cg = codes + (grow0 * (size_t)H + (size_t)n0) * BITS / 8;
-    const uint32_t cpitch = (uint32_t)H * BITS / 8;
-    constexpr int kCodeChunks = kCodeRow / 16;
-#pragma unroll
-    for (int i = 0; i < kTileT * kCodeChunks / kBlockThreads; ++i) {
-        const uint32_t id = (uint32_t)i * kBlockThreads + tid;
-        const uint32_t row = id / kCodeChunks, c = id % kCodeChunks;
-        if ((int)row < rows)
-            stv<u32x4, false>(cg, row * cpitch + c * 16u,
-                              *reinterpret_cast<const u32x4 *>(lc + row * kCodePitch + c * 16u));
-    }
-    uint16_t *sg = s + grow0 * (size_t)Hg + (size_t)(n0 / G);
-    uint16_t *zg = z + grow0 * (size_t)Hg + (size_t)(n0 / G);
-    const uint32_t mpitch = (uint32_t)Hg * 2u;
-    constexpr int kMetaWords = kMetaRow / 4;         // 4-byte pieces of a row
-#pragma unroll
-    for (int i = 0; i < (kTileT * kMetaWords + kBlockThreads - 1) / kBlockThreads; ++i) {
-        const uint32_t id = (uint32_t)i * kBlockThreads + tid;
-        const uint32_t row = id / kMetaWords, c = id % kMetaWords;
-        if ((int)row < rows) {
-            const uint32_t at = row * kMetaRow + c * 4u;
-            stv<uint32_t, false>(sg, row * mpitch + c * 4u, *reinterpret_cast<const uint32_t *>(lsz + at));
-            stv<uint32_t, false>(zg, row * mpitch + c * 4u,
-                                 *reinterpret_cast<const uint32_t *>(lsz + kTileT * kMetaRow + at));
+        // write-out of the tile's live token rows
+        const int rows = min(kTileT, T - t0);
+        const size_t grow0 = (size_t)r * T + (size_t)t0;
+        uint8_t *cg = codes + (grow0 * (size_t)H + (size_t)n0) * BITS / 8;
+        const uint32_t cpitch = (uint32_t)H * BITS / 8;
+        constexpr int kCodeChunks = kCodeRow / 16;
+    #pragma unroll
+        for (int i = 0; i < kTileT * kCodeChunks / kBlockThreads; ++i) {
+            const uint32_t id = (uint32_t)i * kBlockThreads + tid;
+            const uint32_t row = id / kCodeChunks, c = id % kCodeChunks;
+            if ((int)row < rows)
+                stv<u32x4, false>(cg, row * cpitch + c * 16u,
+                                  *reinterpret_cast<const u32x4 *>(lc + row * kCodePitch + c * 16u));
         }
+        uint16_t *sg = s + grow0 * (size_t)Hg + (size_t)(n0 / G);
+        uint16_t *zg = z + grow0 * (size_t)Hg + (size_t)(n0 / G);
+        const uint32_t mpitch = (uint32_t)Hg * 2u;
+        constexpr int kMetaWords = kMetaRow / 4;         // 4-byte pieces of a row
+    #pragma unroll
+        for (int i = 0; i < (kTileT * kMetaWords + kBlockThreads - 1) / kBlockThreads; ++i) {
+            const uint32_t id = (uint32_t)i * kBlockThreads + tid;
+            const uint32_t row = id / kMetaWords, c = id % kMetaWords;
+            if ((int)row < rows) {
+                const uint32_t at = row * kMetaRow + c * 4u;
+                stv<uint32_t, false>(sg, row * mpitch + c * 4u, *reinterpret_cast<const uint32_t *>(lsz + at));
+                stv<uint32_t, false>(zg, row * mpitch + c * 4u,
+                                     *reinterpret_cast<const uint32_t *>(lsz + kTileT * kMetaRow + at));
+            }
+        }
+
+        __syncthreads();   // the next tile's staging overwrites this one's LDS
     }
+}
+
+// Compute units of the current device (one persistent workgroup each),
+// looked up once per device.
+int compute_units() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+    if (cached[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return -1;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 template <int DT, int BITS, int G>
@@ -421,9 +453,12 @@ hipError_t launch_one(const uint16_t *a, const uint16_t *w, int R, int T, int K,
     const int tiles_n = H / kTileN;
     const long long total = (long long)R * tiles_t * tiles_n;
     if (total > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((linear_quantize_kernel<DT, BITS, G>), dim3((unsigned)total),
+    const int cus = compute_units();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    const int grid = (int)(total < cus ? total : cus);
+    hipLaunchKernelGGL((linear_quantize_kernel<DT, BITS, G>), dim3((unsigned)grid),
                        dim3(kBlockThreads), 0, stream, a, w, T, K, H, tiles_t, tiles_n, (int)total,
-                       codes, s, z, y);
+                       grid, codes, s, z, y);
     return hipGetLastError();
 }
 
