@@ -54,6 +54,7 @@ constexpr int kBlk = kWaveSpan / 32;        // 32 x 32 MFMA blocks per wave side
 constexpr int kStage = (kTileN + kTileT) * kTileK;   // 16-bit elements per stage
 constexpr int kGroupT = 4;                  // token tiles per scheduling group
 constexpr int kXcds = 8;
+constexpr int kLdsBytes = 160 * 1024;       // LDS per workgroup on gfx950
 // buffer resource word 3 for raw (untyped, unswizzled) 32-bit-addressed
 // buffers on gfx9-family GPUs
 constexpr int kRawBufferFlags = 0x00020000;
@@ -166,29 +167,54 @@ void linear_quantize_kernel(
     int tiles_t, int tiles_n, int total, int grid, uint8_t *__restrict__ codes,
     uint16_t *__restrict__ s, uint16_t *__restrict__ z, uint16_t *__restrict__ y) {
     static_assert(G >= 8 && G <= kWaveSpan && (G & (G - 1)) == 0, "group of 8..128 channels");
-    __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * kStage];
+    // Epilogue staging: a tile's codes (rows padded by 16 bytes to spread the
+    // LDS banks), then its scales and zeros. When it fits between the last
+    // ring buffer and the end of LDS (4-bit codes, groups of 16 or more), the
+    // next tile's first stages are fetched into ring buffers 0..2 before this
+    // tile's epilogue runs (EARLY); otherwise the staging reuses the ring.
+    constexpr int kCodeRow = kTileN * BITS / 8;      // code bytes of a tile row
+    constexpr int kCodePitch = kCodeRow + 16;
+    constexpr int kMetaRow = kTileN / G * 2;         // bytes of s (or z) of a tile row
+    constexpr int kStagingBytes = kTileT * (kCodePitch + 2 * kMetaRow);
+    constexpr int kRingBytes = kStages * kStage * 2;
+    constexpr bool kEarly = (kStages - 1) * kStage * 2 + kStagingBytes <= kLdsBytes;
+    constexpr int kStagingOff = kEarly ? (kStages - 1) * kStage * 2 : 0;
+    constexpr int kLdsUsed = kStagingOff + kStagingBytes > kRingBytes ? kStagingOff + kStagingBytes
+                                                                      : kRingBytes;
+    static_assert(kLdsUsed <= kLdsBytes && kStagingBytes <= kRingBytes, "staging fits in LDS");
+    __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsUsed / 2];
 
     const uint32_t tid = __builtin_amdgcn_workitem_id_x();
     const int lane = (int)(tid & 63u);
     const int wave = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
     const int wn = wave & 1, wt = wave >> 1;
+    const uint32_t rowb = (uint32_t)K * 2u;          // bytes per operand row
+    const int KT = K / kTileK;
 
-    // Persistent workgroups (`grid` of them, one per CU). Tile order: each XCD (its own L2)
-    // runs a contiguous run of tiles -- workgroup b runs on XCD b % 8 and
-    // takes every (grid/8)-th tile of its XCD's run -- and within a run
-    // kGroupT token tiles x all channel tiles of one rank. A workgroup's
-    // stores of one tile drain while it computes the next.
+    // Persistent workgroups (`grid` of them, one per CU). Tile order: each
+    // XCD (its own L2) runs a contiguous run of tiles -- workgroup b runs on
+    // XCD b % 8 and takes every (grid/8)-th tile of its XCD's run -- and
+    // within a run kGroupT token tiles x all channel tiles of one rank. A
+    // workgroup's stores of one tile drain while it computes the next.
     const int bid = (int)__builtin_amdgcn_workgroup_id_x();
     const bool by_xcd = total % kXcds == 0 && grid % kXcds == 0;
-    for (int it = 0;; ++it) {
+    struct Tile {
+        int r, n0, t0;
+        uint32_t abytes;                 // bytes of the tile's real token rows of A
+        const uint16_t *wb, *ab;         // the tile's first W and A rows
+    };
+    // Tile of iteration `it` of this workgroup; false when there is none.
+    // The A resource covers only the tile's real token rows: rows past T read
+    // as zeros (their outputs are never stored).
+    auto tile_at = [&](int it, Tile &tl) -> bool {
         int logical;
         if (by_xcd) {
             const int slot = it * (grid / kXcds) + bid / kXcds;
-            if (slot >= total / kXcds) break;
+            if (slot >= total / kXcds) return false;
             logical = (bid % kXcds) * (total / kXcds) + slot;
         } else {
             logical = it * grid + bid;
-            if (logical >= total) break;
+            if (logical >= total) return false;
         }
         const int per_rank = tiles_t * tiles_n;
         const int r = logical / per_rank;
@@ -197,102 +223,115 @@ void linear_quantize_kernel(
         const int first_t = grp * kGroupT;
         const int gsize = min(tiles_t - first_t, kGroupT);
         const int in_grp = i - grp * kGroupT * tiles_n;
-        const int tile_t = first_t + in_grp % gsize;
-        const int tile_n = in_grp / gsize;
-        const int n0 = tile_n * kTileN, t0 = tile_t * kTileT;
+        tl.r = r;
+        tl.t0 = (first_t + in_grp % gsize) * kTileT;
+        tl.n0 = (in_grp / gsize) * kTileN;
+        const uint16_t *Wb = W + ((size_t)r * H + tl.n0) * (size_t)K;
+        const uint16_t *Ab = A + ((size_t)r * T + tl.t0) * (size_t)K;
+        tl.abytes = (uint32_t)min(kTileT, T - tl.t0) * rowb;
+        tl.wb = Wb;
+        tl.ab = Ab;
+        return true;
+    };
 
-        const uint16_t *Wb = W + ((size_t)r * H + n0) * (size_t)K;
-        const uint16_t *Ab = A + ((size_t)r * T + t0) * (size_t)K;
-        const uint32_t rowb = (uint32_t)K * 2u;          // bytes per operand row
-
-        // Staging, global -> LDS directly (buffer_load_dwordx4 ... lds: lane i's
-        // 16 bytes land at the instruction's LDS base + 16 i). One instruction
-        // fills 16 staged rows of 64 bytes; lane i serves row i / 4 at chunk
-        // position i % 4, so it fetches the operand's chunk (i % 4) ^ ((row / 4) %
-        // 4) -- the rotation lds_at reads back. Wave w fills rows w*64 .. w*64+63
-        // of both tiles (4 instructions each, 8 per stage). Addresses are a
-        // buffer resource per operand tile (SGPRs), a fixed 32-bit lane offset and
-        // the stage's k offset as the scalar offset. The A resource covers only
-        // the tile's real token rows: rows past T read as zeros (their outputs are
-        // never stored).
-        constexpr int kLoadsPerStage = 8;            // per wave
-        const uint32_t lrow = (uint32_t)lane >> 2;   // row within the instruction's 16
-        const uint32_t lchunk = ((uint32_t)lane & 3u) ^ ((lrow >> 2) & 3u);
-        const uint32_t wrow0 = (uint32_t)wave * 64u;
-        const int t_rows = min(kTileT, T - t0);
+    // Staging, global -> LDS directly (buffer_load_dwordx4 ... lds: lane i's
+    // 16 bytes land at the instruction's LDS base + 16 i). One instruction
+    // fills 16 staged rows of 64 bytes; lane i serves row i / 4 at chunk
+    // position i % 4, so it fetches the operand's chunk (i % 4) ^ ((row / 4) %
+    // 4) -- the rotation lds_at reads back. Wave w fills rows w*64 .. w*64+63
+    // of both tiles (4 instructions each, 8 per stage). Addresses are the
+    // tile's buffer resources (SGPRs), a fixed 32-bit lane offset and the
+    // stage's k offset as the scalar offset.
+    constexpr int kLoadsPerStage = 8;            // per wave
+    const uint32_t lrow = (uint32_t)lane >> 2;   // row within the instruction's 16
+    const uint32_t lchunk = ((uint32_t)lane & 3u) ^ ((lrow >> 2) & 3u);
+    const uint32_t wrow0 = (uint32_t)wave * 64u;
+    const uint32_t voff = (wrow0 + lrow) * rowb + lchunk * 16u;   // + 16 j rows
+    // the two loads (W and A rows wrow0 + 16 j ..) of part j of stage kt
+    auto stage_in_part = [&](const Tile &tl, int kt, int j) {
+        const int kb = kt * (kTileK * 2);
+        uint16_t *sw = lds + (kt % kStages) * kStage;
+        uint16_t *sa = sw + kTileN * kTileK;
+        const uint32_t lrow0 = (wrow0 + 16u * j) * kTileK;   // wave-uniform
+        const uint32_t vo = voff + 16u * j * rowb;
         const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(Wb), (short)0, (int)(kTileN * rowb), kRawBufferFlags);
+            const_cast<uint16_t *>(tl.wb), (short)0, (int)(kTileN * rowb), kRawBufferFlags);
         const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(Ab), (short)0, (int)((uint32_t)t_rows * rowb), kRawBufferFlags);
-        const uint32_t voff = (wrow0 + lrow) * rowb + lchunk * 16u;   // + 16 j rows
-        // the two loads (W and A rows wrow0 + 16 j ..) of part j of stage kt
-        auto stage_in_part = [&](int kt, int j) {
-            const int kb = kt * (kTileK * 2);
-            uint16_t *sw = lds + (kt % kStages) * kStage;
-            uint16_t *sa = sw + kTileN * kTileK;
-            const uint32_t lrow0 = (wrow0 + 16u * j) * kTileK;   // wave-uniform
-            const uint32_t vo = voff + 16u * j * rowb;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                wres, (__attribute__((address_space(3))) void *)(sw + lrow0), 16, vo, kb, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ares, (__attribute__((address_space(3))) void *)(sa + lrow0), 16, vo, kb, 0, 0);
-        };
-        auto stage_in = [&](int kt) {
-    #pragma unroll
-            for (int j = 0; j < 4; ++j) stage_in_part(kt, j);
-        };
+            const_cast<uint16_t *>(tl.ab), (short)0, (int)tl.abytes, kRawBufferFlags);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wres, (__attribute__((address_space(3))) void *)(sw + lrow0), 16, vo, kb, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ares, (__attribute__((address_space(3))) void *)(sa + lrow0), 16, vo, kb, 0, 0);
+    };
+    auto stage_in = [&](const Tile &tl, int kt) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) stage_in_part(tl, kt, j);
+    };
+    // the first min(KT, kStages - 1) stages of a tile
+    auto prologue_issue = [&](const Tile &tl) {
+        stage_in(tl, 0);
+        if (KT > 1) stage_in(tl, 1);
+        if (KT > 2) stage_in(tl, 2);
+    };
 
-        // fragment reads: row (block base + lane % 32), chunk 2 ks + lane / 32
-        const uint32_t frow = (uint32_t)lane & 31u, fhalf = (uint32_t)lane >> 5;
-        // fragments b (W rows and A rows of block b) of step ks of stage kt
-        auto frag_part = [&](int kt, int ks, int b, u32x4 (&fw)[kBlk], u32x4 (&fa)[kBlk]) {
-            const uint16_t *sw = lds + (kt % kStages) * kStage;
-            const uint16_t *sa = sw + kTileN * kTileK;
-            const uint32_t c = 2u * ks + fhalf;
-            fw[b] = *reinterpret_cast<const u32x4 *>(sw + lds_at(wn * kWaveSpan + b * 32 + frow, c));
-            fa[b] = *reinterpret_cast<const u32x4 *>(sa + lds_at(wt * kWaveSpan + b * 32 + frow, c));
-        };
-        auto frags = [&](int kt, int ks, u32x4 (&fw)[kBlk], u32x4 (&fa)[kBlk]) {
-    #pragma unroll
-            for (int b = 0; b < kBlk; ++b) frag_part(kt, ks, b, fw, fa);
-        };
+    // fragment reads: row (block base + lane % 32), chunk 2 ks + lane / 32
+    const uint32_t frow = (uint32_t)lane & 31u, fhalf = (uint32_t)lane >> 5;
+    // fragments b (W rows and A rows of block b) of step ks of stage kt
+    auto frag_part = [&](int kt, int ks, int b, u32x4 (&fw)[kBlk], u32x4 (&fa)[kBlk]) {
+        const uint16_t *sw = lds + (kt % kStages) * kStage;
+        const uint16_t *sa = sw + kTileN * kTileK;
+        const uint32_t c = 2u * ks + fhalf;
+        fw[b] = *reinterpret_cast<const u32x4 *>(sw + lds_at(wn * kWaveSpan + b * 32 + frow, c));
+        fa[b] = *reinterpret_cast<const u32x4 *>(sa + lds_at(wt * kWaveSpan + b * 32 + frow, c));
+    };
+    auto frags = [&](int kt, int ks, u32x4 (&fw)[kBlk], u32x4 (&fa)[kBlk]) {
+#pragma unroll
+        for (int b = 0; b < kBlk; ++b) frag_part(kt, ks, b, fw, fa);
+    };
 
+    Tile cur;
+    if (!tile_at(0, cur)) return;
+    prologue_issue(cur);
+    for (int it = 0;; ++it) {
         f32x16 acc[kBlk][kBlk];
-    #pragma unroll
+#pragma unroll
         for (int a = 0; a < kBlk; ++a)
-    #pragma unroll
+#pragma unroll
             for (int b = 0; b < kBlk; ++b) acc[a][b] = f32x16{};
 
         // One stage = 2 steps of k = 16, 16 MFMAs each, over an LDS ring of
-        // kStages buffers. At stage kt the loads of stage kt + kStages - 1 go out
-        // (into the buffer stage kt - 1 used); step 0's MFMAs overlap the reads of
-        // step 1's fragments; then this wave waits until its loads of stage kt + 1
-        // have landed (the later stages' loads stay in flight) and the workgroup
-        // barrier publishes stage kt + 1; step 1's MFMAs overlap the reads of its
-        // first fragments. Every read of a buffer happens before the barrier that
-        // precedes its refill.
+        // kStages buffers. At stage kt the loads of stage kt + kStages - 1 go
+        // out (into the buffer stage kt - 1 used); step 0's MFMAs overlap the
+        // reads of step 1's fragments; then this wave waits until its loads
+        // of stage kt + 1 have landed (the later stages' loads stay in flight)
+        // and the workgroup barrier publishes stage kt + 1; step 1's MFMAs
+        // overlap the reads of its first fragments. Every read of a buffer
+        // happens before the barrier that precedes its refill. (Loads complete
+        // in order, so these vmcnt bounds hold even with the previous tile's
+        // stores still in flight: those only add younger or older stores.)
         u32x4 fw[2][kBlk], fa[2][kBlk];
         // A step in four chunks: chunk nb = the 4 MFMAs of W block nb, then
-        // `side(nb)` (the LDS reads and staging loads that overlap them); nothing
-        // moves across chunks, so the loads are spread between the MFMAs.
+        // `side(nb)` (the LDS reads and staging loads that overlap them);
+        // nothing moves across chunks, so the loads are spread between the
+        // MFMAs.
         auto step = [&](int ks, auto &&side) {
-    #pragma unroll
+#pragma unroll
             for (int nb = 0; nb < kBlk; ++nb) {
-    #pragma unroll
+#pragma unroll
                 for (int tb = 0; tb < kBlk; ++tb)
                     acc[nb][tb] = mfma<DT>(fw[ks & 1][nb], fa[ks & 1][tb], acc[nb][tb]);
                 side(nb);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        // ISSUE: stage kt + kStages - 1 exists; PEND: stages issued after kt + 1
-        // (0, 1 or 2 -- they may stay in flight); LAST: no stage follows
+        // ISSUE: stage kt + kStages - 1 exists; PEND: stages issued after
+        // kt + 1 (0, 1 or 2 -- they may stay in flight); LAST: no stage follows
         auto stage = [&](int kt, auto issue_tag, auto pend_tag, auto last_tag) {
             constexpr bool ISSUE = decltype(issue_tag)::value;
             constexpr int PEND = decltype(pend_tag)::value;
             constexpr bool LAST = decltype(last_tag)::value;
             step(0, [&](int nb) {
-                if constexpr (ISSUE) stage_in_part(kt + kStages - 1, nb);
+                if constexpr (ISSUE) stage_in_part(cur, kt + kStages - 1, nb);
                 frag_part(kt, 1, nb, fw[1], fa[1]);
             });
             if constexpr (!LAST) {
@@ -309,11 +348,7 @@ void linear_quantize_kernel(
         using P1 = std::integral_constant<int, 1>;
         using P2 = std::integral_constant<int, 2>;
 
-        const int KT = K / kTileK;
-        // prologue: the first min(KT, kStages - 1) stages; wait for stage 0
-        stage_in(0);
-        if (KT > 1) stage_in(1);
-        if (KT > 2) stage_in(2);
+        // the tile's first stages are in flight: wait for stage 0
         if (KT > 2) wait_loads<2 * kLoadsPerStage>();
         else if (KT > 1) wait_loads<kLoadsPerStage>();
         else wait_loads<0>();
@@ -324,24 +359,27 @@ void linear_quantize_kernel(
         if (KT >= 2) stage(KT - 2, F_{}, P0{}, F_{});
         stage(KT - 1, F_{}, P0{}, T_{});
 
+        __syncthreads();   // every wave has read its last operand fragments
+        Tile nxt;
+        const bool more = tile_at(it + 1, nxt);
+        if constexpr (kEarly) {
+            if (more) prologue_issue(nxt);
+        }
+
         // ---- epilogue: round to the dtype, quantize per (token, group) ----
         // Run j = 4 nb + m of a lane holds channels nb*32 + 8m + 4*(lane/32) + 0..3
         // of the wave's span (accumulator entries 4m..4m+3 of block nb); a group
         // of G channels is RG = G/8 consecutive runs of each lane of the pair.
-        // Codes, scales and zeros of the whole tile are first gathered in LDS (the
-        // operand buffers are free by then) and then written out row by row in
-        // 16-byte pieces: a token row of the tile is one contiguous run of codes.
+        // Codes, scales and zeros of the whole tile are first gathered in LDS
+        // (kStagingOff) and then written out row by row in 16-byte pieces: a
+        // token row of the tile is one contiguous run of codes.
         constexpr int RG = G / 8;
-        constexpr int kCodeRow = kTileN * BITS / 8;      // code bytes of a tile row
-        constexpr int kCodePitch = kCodeRow + 16;        // padded (spreads LDS banks)
-        constexpr int kMetaRow = kTileN / G * 2;         // bytes of s (or z) of a tile row
-        static_assert(kTileT * (kCodePitch + 2 * kMetaRow) <= kStages * kStage * 2, "tile fits in LDS");
-        uint8_t *lc = reinterpret_cast<uint8_t *>(lds);
+        uint8_t *lc = reinterpret_cast<uint8_t *>(lds) + kStagingOff;
         uint8_t *lsz = lc + kTileT * kCodePitch;         // s rows, then z rows
         const int Hg = H / G;
         const uint32_t h4 = 4u * fhalf;
         const uint32_t lane_y = frow * (uint32_t)H * 2u;
-        __syncthreads();   // every wave has read its last operand fragments
+        const int r = cur.r, n0 = cur.n0, t0 = cur.t0;
     #pragma unroll
         for (int tb = 0; tb < kBlk; ++tb) {
             const uint32_t tl = (uint32_t)(wt * kWaveSpan + tb * 32) + frow;   // token in the tile
@@ -395,7 +433,10 @@ void linear_quantize_kernel(
                 }
             }
         }
-        __syncthreads();
+        // this wave's LDS writes are done (the next tile's staging loads may
+        // stay in flight), then every wave's
+        wait_loads<63>();
+        barrier_keep_loads();
 
         // write-out of the tile's live token rows
         const int rows = min(kTileT, T - t0);
@@ -427,7 +468,11 @@ void linear_quantize_kernel(
             }
         }
 
-        __syncthreads();   // the next tile's staging overwrites this one's LDS
+        wait_loads<63>();   // the staging area has been read out by every wave
+        barrier_keep_loads();
+        if (!more) break;
+        if constexpr (!kEarly) prologue_issue(nxt);
+        cur = nxt;
     }
 }
 
