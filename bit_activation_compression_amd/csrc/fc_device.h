@@ -34,6 +34,7 @@ constexpr int kWavesPerBlock = kBlockThreads / kWave;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -61,6 +62,28 @@ __device__ __forceinline__ uint64_t wave_index() {
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     asm("" : "+v"(v));
     return v;
+}
+
+// A wave-uniform global-memory base pinned in scalar registers, and loads
+// and stores at that base plus a 32-bit per-lane byte offset. Without the
+// pin the compiler may reassociate (uniform base + per-lane offset) +
+// uniform offset into 64-bit per-lane address arithmetic; pinned, every
+// access takes the scalar-base + 32-bit lane offset form.
+#define FC_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ FC_GLOBAL T *sgpr_ptr(T *p) {
+    asm("" : "+s"(p));
+    return (FC_GLOBAL T *)p;
+}
+
+template <typename V>
+__device__ __forceinline__ V ldg(const FC_GLOBAL void *base, uint32_t byte_off) {
+    return *(const FC_GLOBAL V *)((const FC_GLOBAL uint8_t *)base + byte_off);
+}
+
+template <typename V>
+__device__ __forceinline__ void stg(FC_GLOBAL void *base, uint32_t byte_off, V v) {
+    *(FC_GLOBAL V *)((FC_GLOBAL uint8_t *)base + byte_off) = v;
 }
 
 // Pins v as a rounded binary32 register value. Without it the compiler may
@@ -219,7 +242,10 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx) {
 // Codes of the lane's 8 values: q = clamp(round_half_even(fp32(fp32(v - z) *
 // inv)), 0, Q). v_cvt_pk_u8_f32 rounds to nearest even and saturates to
 // [0, 255] while inserting the byte (checked on the GPU), so 8-bit codes need
-// no separate clamp; 4-bit codes are clamped to [0, 15] first (v_med3_f32).
+// no separate clamp. 4-bit codes are converted the same way into bytes 0 and
+// 2 of four words (elements k and 4 + k in word k), clamped to 15 two at a
+// time (v_pk_min_u16; clamping the rounded value equals rounding the clamped
+// one, the bounds being integers) and then interleaved as nibbles.
 // Layout: 4-bit codes in one word, element 2i in the low nibble of byte i;
 // 8-bit codes in two words, element i in byte i.
 template <int BITS>
@@ -237,17 +263,17 @@ __device__ __forceinline__ void encode8(const float (&v)[kLaneElems], const Grou
             w[k] = __builtin_amdgcn_cvt_pk_u8_f32(t[4 * k + 3], 3, a);
         }
     } else {
+        uint32_t c[4];
 #pragma unroll
-        for (int i = 0; i < kLaneElems; ++i) t[i] = __builtin_amdgcn_fmed3f(t[i], 0.0f, 15.0f);
-        uint32_t ev = __builtin_amdgcn_cvt_pk_u8_f32(t[0], 0, 0u);   // even elements
-        ev = __builtin_amdgcn_cvt_pk_u8_f32(t[2], 1, ev);
-        ev = __builtin_amdgcn_cvt_pk_u8_f32(t[4], 2, ev);
-        ev = __builtin_amdgcn_cvt_pk_u8_f32(t[6], 3, ev);
-        uint32_t od = __builtin_amdgcn_cvt_pk_u8_f32(t[1], 0, 0u);   // odd elements
-        od = __builtin_amdgcn_cvt_pk_u8_f32(t[3], 1, od);
-        od = __builtin_amdgcn_cvt_pk_u8_f32(t[5], 2, od);
-        od = __builtin_amdgcn_cvt_pk_u8_f32(t[7], 3, od);
-        w[0] = ev | (od << 4);
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t b = __builtin_amdgcn_cvt_pk_u8_f32(t[4 + k], 2,
+                                                              __builtin_amdgcn_cvt_pk_u8_f32(t[k], 0, 0u));
+            const u16x2 m = __builtin_elementwise_min(__builtin_bit_cast(u16x2, b), u16x2{15, 15});
+            c[k] = __builtin_bit_cast(uint32_t, m);
+        }
+        // three v_lshl_or_b32 (opaque keeps the compiler from reassociating)
+        const uint32_t h = opaque((opaque((c[3] << 4) | c[2]) << 4) | c[1]);
+        w[0] = (h << 4) | c[0];
     }
 }
 
@@ -278,47 +304,45 @@ __device__ __forceinline__ void decode8(const uint32_t (&w)[BITS == 4 ? 1 : 2], 
 }
 
 // Dequantized values x_k = fp32(q_k * s + z) of 8 codes, for a scale s and
-// zero z given as fp16 bit patterns. The codes are spread into the 16-bit
-// halves of four registers (one mask, or a shift and a mask, per register);
-// read as fp16, a half holding the integer q is the subnormal q * 2^-24,
-// exactly. One mixed-precision fma per value (v_fma_mix_f32: the fp16 half
-// selected in place, the binary32 scale s * 2^24, the fp16 zero) then forms
-// (q * 2^-24) * (s * 2^24) + z: the product is the exact q*s (at most 8 x 11
-// significant bits) and the sum is rounded once, exactly as fp32(q*s + z).
+// zero z given as fp16 bit patterns. Each code is isolated inside a 16-bit
+// half of a register, at bits 0..7 or, for the high nibble of a 4-bit pair,
+// at bits 4..7; read as fp16, such a half is the subnormal q * 2^-24 or
+// q * 2^-20, exactly. One mixed-precision fma per value (v_fma_mix_f32: the
+// fp16 half selected in place, the binary32 scale s * 2^24 or s * 2^20, the
+// fp16 zero) then forms q * s + z with the exact product (at most 8 x 11
+// significant bits) and one rounding, exactly as fp32(q*s + z). Unpacking
+// takes 5 bit operations per 8 four-bit codes and 4 per 8 eight-bit codes.
 // This needs fp16 subnormals preserved on input (they are: the build keeps
 // the default denormal mode, checked by the instruction guard test).
 template <int BITS>
 __device__ __forceinline__ void dequant8(const uint32_t (&w)[BITS == 4 ? 1 : 2], uint16_t s16,
                                          uint16_t z16, float (&x)[kLaneElems]) {
-    uint32_t p[4];
-    int e_lo[4], e_hi[4];   // elements held in the low and high halves of p[i]
+    const float s = (float)__builtin_bit_cast(_Float16, s16);
+    const float sc24 = s * 16777216.0f;   // s * 2^24, exact
+    const float z = (float)__builtin_bit_cast(_Float16, z16);
+    // the two values whose codes sit in the halves of p
+    auto pair = [&](uint32_t p, float sc, int e_lo, int e_hi) {
+        const f16x2 h = __builtin_bit_cast(f16x2, p);
+        x[e_lo] = __builtin_fmaf((float)h.x, sc, z);
+        x[e_hi] = __builtin_fmaf((float)h.y, sc, z);
+    };
     if constexpr (BITS == 4) {
-        // byte i = q(2i) | q(2i+1) << 4: bits 4k of each 16-bit half are elements k, 4 + k
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            p[k] = (w[0] >> (4 * k)) & 0x000F000Fu;
-            e_lo[k] = k;
-            e_hi[k] = 4 + k;
-        }
+        // byte i = q(2i) | q(2i+1) << 4: the low half holds elements 0..3,
+        // the high half 4..7, as nibbles at bits 0, 4, 8, 12
+        const float sc20 = s * 1048576.0f;   // s * 2^20, exact
+        const uint32_t w8 = w[0] >> 8;
+        pair(w[0] & 0x000F000Fu, sc24, 0, 4);
+        pair(w[0] & 0x00F000F0u, sc20, 1, 5);
+        pair(w8 & 0x000F000Fu, sc24, 2, 6);
+        pair(w8 & 0x00F000F0u, sc20, 3, 7);
     } else {
-        // word j holds elements 4j..4j+3, one per byte
+        // word j holds elements 4j..4j+3, one per byte; v_perm_b32 moves
+        // bytes 1 and 3 to bytes 0 and 2 and zeroes the others
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            p[2 * j] = w[j] & 0x00FF00FFu;
-            p[2 * j + 1] = (w[j] >> 8) & 0x00FF00FFu;
-            e_lo[2 * j] = 4 * j;
-            e_hi[2 * j] = 4 * j + 2;
-            e_lo[2 * j + 1] = 4 * j + 1;
-            e_hi[2 * j + 1] = 4 * j + 3;
+            pair(w[j] & 0x00FF00FFu, sc24, 4 * j, 4 * j + 2);
+            pair(__builtin_amdgcn_perm(w[j], w[j], 0x0C030C01u), sc24, 4 * j + 1, 4 * j + 3);
         }
-    }
-    const float sc = (float)__builtin_bit_cast(_Float16, s16) * 16777216.0f;   // s * 2^24, exact
-    const float z = (float)__builtin_bit_cast(_Float16, z16);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const f16x2 h = __builtin_bit_cast(f16x2, p[k]);
-        x[e_lo[k]] = __builtin_fmaf((float)h.x, sc, z);
-        x[e_hi[k]] = __builtin_fmaf((float)h.y, sc, z);
     }
 }
 

@@ -167,6 +167,16 @@ RAGGED = [
     (2, 3, 2048, 8, 256, synth.BF16),
     (8, 2, 1024, 4, 128, synth.F16),
     (4, 129, 4096, 8, 4096, synth.BF16),
+    # n = T*H not a multiple of 32: the last lane's run of 32 positions ends
+    # after 8, 16 or 24 of them (stage-2 groups of 8 or 16)
+    (1, 3, 40, 4, 8, synth.F16),
+    (1, 3, 48, 8, 16, synth.BF16),
+    (2, 5, 48, 4, 8, synth.BF16),
+    (2, 5, 48, 8, 8, synth.F16),
+    (3, 3, 24, 8, 8, synth.F16),
+    # stage-2 groups of 8192: one group spans four wave slots
+    (1, 2, 8192, 4, 8192, synth.F16),
+    (2, 3, 16384, 8, 8192, synth.BF16),
 ]
 
 
@@ -255,7 +265,7 @@ def test_mixed_widths(name, bits, bits2):
 
 
 @pytest.mark.parametrize("R,T,H,group", [(3, 7, 384, 128), (8, 9, 8192, 8192), (2, 33, 1024, 8),
-                                         (5, 3, 640, 128), (6, 11, 3072, 512)])
+                                         (5, 3, 640, 128), (6, 11, 3072, 512), (2, 5, 48, 8)])
 def test_mixed_widths_ragged(R, T, H, group):
     for bits, bits2 in ((4, 8), (8, 4)):
         w = synth.workload("tiny").with_(R=R, T=T, H=H, bits=bits, group=group, dtype=synth.BF16,
