@@ -64,6 +64,14 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     return v;
 }
 
+// A fresh copy of v that the compiler cannot hoist out of a loop (volatile
+// asm, no instruction emitted): values derived from it are recomputed where
+// they are used instead of being kept live across the whole loop.
+__device__ __forceinline__ uint32_t fresh(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 // A wave-uniform global-memory base pinned in scalar registers, and loads
 // and stores at that base plus a 32-bit per-lane byte offset. Without the
 // pin the compiler may reassociate (uniform base + per-lane offset) +

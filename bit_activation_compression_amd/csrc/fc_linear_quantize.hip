@@ -24,11 +24,14 @@
 //     group (<= 128 consecutive channels of one token) lies in one lane pair
 //     (lane, lane ^ 32), half in each, and its minimum and maximum need one
 //     v_permlane32_swap after the in-lane reduction;
-//   - K is walked in stages of 32: both 256 x 32 operand tiles are staged in
-//     an LDS ring of 4 stages (128 KiB) straight from global memory
-//     (global_load_lds), three stages ahead of the matrix cores; each 64-byte
-//     row's four 16-byte chunks are rotated by (row / 4) % 4 so that the
-//     fragment reads (32 rows x one chunk) are free of bank conflicts;
+//   - K is walked in stages of 32, staged in pairs: both 256 x 64 operand
+//     tiles of a pair of stages go to one of two LDS buffers (2 x 64 KiB)
+//     straight from global memory (buffer_load ... lds), a pair ahead of the
+//     matrix cores. A staged row is 64 k values = 128 bytes, one whole L2
+//     line per row and load, so the operand traffic reaches L2 as full-line
+//     requests; each row's eight 16-byte chunks are rotated by (row / 2) % 8
+//     so that the fragment reads (32 rows x one chunk) are free of bank
+//     conflicts;
 //   - one persistent workgroup per CU walks its tiles; each XCD (its own L2)
 //     runs a contiguous run of tiles, ordered 4 token tiles x all channel
 //     tiles, so that concurrently running workgroups share their A and W
@@ -47,11 +50,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTileN = 256;                 // output channels per workgroup
 constexpr int kTileT = 256;                 // tokens per workgroup
-constexpr int kTileK = 32;                  // k per LDS stage
-constexpr int kStages = 4;                  // LDS ring; loads run kStages - 1 stages ahead
+constexpr int kTileK = 32;                  // k per stage (2 MFMA steps of 16)
+constexpr int kPairK = 2 * kTileK;          // k per staged pair of stages (128-byte rows)
+constexpr int kPairs = 2;                   // LDS buffers, one pair each
 constexpr int kWaveSpan = 128;              // channels (and tokens) per wave
 constexpr int kBlk = kWaveSpan / 32;        // 32 x 32 MFMA blocks per wave side
-constexpr int kStage = (kTileN + kTileT) * kTileK;   // 16-bit elements per stage
+constexpr int kWPair = kTileN * kPairK;               // elements of one pair's W tile
+constexpr int kPair = (kTileN + kTileT) * kPairK;    // 16-bit elements per pair buffer (W, then A)
 constexpr int kGroupT = 4;                  // token tiles per scheduling group
 constexpr int kXcds = 8;
 constexpr int kLdsBytes = 160 * 1024;       // LDS per workgroup on gfx950
@@ -69,13 +74,6 @@ __device__ __forceinline__ f32x16 mfma(const u32x4 &a, const u32x4 &b, const f32
     else
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
-// Element offset of 16-byte chunk c (0..3) of staged row `row` (64 bytes):
-// chunks are rotated by (row / 4) % 4, so that any 8 consecutive rows read at
-// one chunk index cover all 64 LDS banks once.
-__device__ __forceinline__ uint32_t lds_at(uint32_t row, uint32_t c) {
-    return row * kTileK + ((c ^ ((row >> 2) & 3u)) << 3);
 }
 
 // s_waitcnt until at most N vector-memory operations of this wave are
@@ -168,17 +166,17 @@ void linear_quantize_kernel(
     uint16_t *__restrict__ s, uint16_t *__restrict__ z, uint16_t *__restrict__ y) {
     static_assert(G >= 8 && G <= kWaveSpan && (G & (G - 1)) == 0, "group of 8..128 channels");
     // Epilogue staging: a tile's codes (rows padded by 16 bytes to spread the
-    // LDS banks), then its scales and zeros. When it fits between the last
-    // ring buffer and the end of LDS (4-bit codes, groups of 16 or more), the
-    // next tile's first stages are fetched into ring buffers 0..2 before this
-    // tile's epilogue runs (EARLY); otherwise the staging reuses the ring.
+    // LDS banks), then its scales and zeros. When it fits between the first
+    // pair buffer and the end of LDS (all but 8-bit codes in groups of 8), the
+    // next tile's first pair is fetched into buffer 0 before this tile's
+    // epilogue runs (EARLY); otherwise the staging reuses the buffers.
     constexpr int kCodeRow = kTileN * BITS / 8;      // code bytes of a tile row
     constexpr int kCodePitch = kCodeRow + 16;
     constexpr int kMetaRow = kTileN / G * 2;         // bytes of s (or z) of a tile row
     constexpr int kStagingBytes = kTileT * (kCodePitch + 2 * kMetaRow);
-    constexpr int kRingBytes = kStages * kStage * 2;
-    constexpr bool kEarly = (kStages - 1) * kStage * 2 + kStagingBytes <= kLdsBytes;
-    constexpr int kStagingOff = kEarly ? (kStages - 1) * kStage * 2 : 0;
+    constexpr int kRingBytes = kPairs * kPair * 2;
+    constexpr bool kEarly = kPair * 2 + kStagingBytes <= kLdsBytes;
+    constexpr int kStagingOff = kEarly ? kPair * 2 : 0;
     constexpr int kLdsUsed = kStagingOff + kStagingBytes > kRingBytes ? kStagingOff + kStagingBytes
                                                                       : kRingBytes;
     static_assert(kLdsUsed <= kLdsBytes && kStagingBytes <= kRingBytes, "staging fits in LDS");
@@ -189,7 +187,8 @@ void linear_quantize_kernel(
     const int wave = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
     const int wn = wave & 1, wt = wave >> 1;
     const uint32_t rowb = (uint32_t)K * 2u;          // bytes per operand row
-    const int KT = K / kTileK;
+    const int KT = K / kTileK;                       // stages
+    const int KP = (KT + 1) / 2;                     // staged pairs (the last may be half used)
 
     // Persistent workgroups (`grid` of them, one per CU). Tile order: each
     // XCD (its own L2) runs a contiguous run of tiles -- workgroup b runs on
@@ -236,62 +235,95 @@ void linear_quantize_kernel(
 
     // Staging, global -> LDS directly (buffer_load_dwordx4 ... lds: lane i's
     // 16 bytes land at the instruction's LDS base + 16 i). One instruction
-    // fills 16 staged rows of 64 bytes; lane i serves row i / 4 at chunk
-    // position i % 4, so it fetches the operand's chunk (i % 4) ^ ((row / 4) %
-    // 4) -- the rotation lds_at reads back. Wave w fills rows w*64 .. w*64+63
-    // of both tiles (4 instructions each, 8 per stage). Addresses are the
-    // tile's buffer resources (SGPRs), a fixed 32-bit lane offset and the
-    // stage's k offset as the scalar offset.
-    constexpr int kLoadsPerStage = 8;            // per wave
-    const uint32_t lrow = (uint32_t)lane >> 2;   // row within the instruction's 16
-    const uint32_t lchunk = ((uint32_t)lane & 3u) ^ ((lrow >> 2) & 3u);
+    // fills 8 staged rows of 128 bytes; lane i serves row i / 8 at chunk
+    // position i % 8, so it fetches the operand's chunk (i % 8) ^ ((row / 2) %
+    // 8) -- the rotation lds_at reads back. Wave w fills rows w*64 .. w*64+63
+    // of both tiles (8 instructions each, 16 per pair). Addresses are the
+    // tile's buffer resources (SGPRs), a 32-bit lane offset (one for even and
+    // one for odd instructions: the rotation of row w*64 + 8j + i/8 is
+    // (4 (j % 2) + i/16) % 8) and, as the scalar offset, the pair's k offset
+    // plus the instruction's 8 j rows. The last pair of an odd stage count
+    // also fetches k values past the row's end: those bytes belong to the
+    // next row, or lie past the resource and read as zeros, and are never
+    // used.
+    constexpr int kLoadsPerPair = 16;            // per wave
     const uint32_t wrow0 = (uint32_t)wave * 64u;
-    const uint32_t voff = (wrow0 + lrow) * rowb + lchunk * 16u;   // + 16 j rows
-    // the two loads (W and A rows wrow0 + 16 j ..) of part j of stage kt
-    auto stage_in_part = [&](const Tile &tl, int kt, int j) {
-        const int kb = kt * (kTileK * 2);
-        uint16_t *sw = lds + (kt % kStages) * kStage;
-        uint16_t *sa = sw + kTileN * kTileK;
-        const uint32_t lrow0 = (wrow0 + 16u * j) * kTileK;   // wave-uniform
-        const uint32_t vo = voff + 16u * j * rowb;
+    // Per-lane offsets of the staging loads and of the fragment reads (below).
+    // They are recomputed from the lane id for every tile and before every
+    // batch of staging loads (`fresh` keeps the compiler from hoisting them),
+    // so that none of them is live across the epilogue, which needs nearly all
+    // of the registers.
+    struct LaneOffs {
+        uint32_t voff_even, voff_odd;   // staging loads: lane offset of even / odd instructions
+        uint32_t cx0, cx1;              // fragment reads: rotated chunk offset of steps 0 / 1
+        uint32_t fbw, fba;              // fragment reads: the wave's W and A row bases (bytes)
+    };
+    auto lane_offs = [&]() {
+        const uint32_t l = fresh((uint32_t)lane);
+        LaneOffs o;
+        const uint32_t lrow = l >> 3;            // row within a staging instruction's 8
+        const uint32_t lpos = l & 7u;            // 16-byte position within the staged row
+        const uint32_t vrow = (wrow0 + lrow) * rowb;
+        o.voff_even = vrow + ((lpos ^ ((lrow >> 1) & 7u)) << 4);
+        o.voff_odd = vrow + ((lpos ^ ((4u + (lrow >> 1)) & 7u)) << 4);
+        const uint32_t frow = l & 31u, fhalf = l >> 5;
+        const uint32_t rotx = fhalf ^ ((frow >> 1) & 7u);
+        o.cx0 = rotx << 4;
+        o.cx1 = (rotx ^ 2u) << 4;
+        o.fbw = (uint32_t)(wn * kWaveSpan + frow) * (kPairK * 2);
+        o.fba = kWPair * 2 + (uint32_t)(wt * kWaveSpan + frow) * (kPairK * 2);
+        return o;
+    };
+    // part nb (0..3) of pair p: instructions j = 2 nb, 2 nb + 1 of both operands
+    auto pair_in_part = [&](const LaneOffs &lo, const Tile &tl, int p, int nb) {
+        uint16_t *sw = lds + (p & 1) * kPair;
+        uint16_t *sa = sw + kWPair;
         const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t *>(tl.wb), (short)0, (int)(kTileN * rowb), kRawBufferFlags);
         const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t *>(tl.ab), (short)0, (int)tl.abytes, kRawBufferFlags);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            wres, (__attribute__((address_space(3))) void *)(sw + lrow0), 16, vo, kb, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ares, (__attribute__((address_space(3))) void *)(sa + lrow0), 16, vo, kb, 0, 0);
-    };
-    auto stage_in = [&](const Tile &tl, int kt) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) stage_in_part(tl, kt, j);
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * nb + jj;
+            const uint32_t l0 = (wrow0 + 8u * j) * kPairK;                // wave-uniform
+            const int so = p * (kPairK * 2) + 8 * j * (int)rowb;
+            // (a named value: a conditional expression written as the
+            // builtin's argument makes the host pass drop the launch stub)
+            const uint32_t vo = jj ? lo.voff_odd : lo.voff_even;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wres, (__attribute__((address_space(3))) void *)(sw + l0), 16, vo, so, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ares, (__attribute__((address_space(3))) void *)(sa + l0), 16, vo, so, 0, 0);
+        }
     };
-    // the first min(KT, kStages - 1) stages of a tile
-    auto prologue_issue = [&](const Tile &tl) {
-        stage_in(tl, 0);
-        if (KT > 1) stage_in(tl, 1);
-        if (KT > 2) stage_in(tl, 2);
+    auto pair_in = [&](const Tile &tl, int p) {
+        const LaneOffs lo = lane_offs();
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) pair_in_part(lo, tl, p, nb);
     };
 
-    // fragment reads: row (block base + lane % 32), chunk 2 ks + lane / 32
-    const uint32_t frow = (uint32_t)lane & 31u, fhalf = (uint32_t)lane >> 5;
+    // fragment reads: row (block base + lane % 32), chunk 4 h + 2 ks + lane / 32
+    // for step ks of stage kt = 2 p + h (half h of pair p). The rotation of a
+    // fragment row, (row / 2) % 8, is (lane % 32 / 2) % 8 for every block, and
+    // the chunk's three bits are h, ks and lane / 32, so the rotated chunk is
+    // (4 h) ^ (2 ks) ^ rotx: a read is the wave's W or A row base, plus the
+    // per-lane chunk offset of ks XOR the stage's half bit (64 bytes), plus
+    // the pair buffer's and the block's offsets.
+    const uint8_t *lbytes = reinterpret_cast<const uint8_t *>(lds);
     // fragments b (W rows and A rows of block b) of step ks of stage kt
-    auto frag_part = [&](int kt, int ks, int b, u32x4 (&fw)[kBlk], u32x4 (&fa)[kBlk]) {
-        const uint16_t *sw = lds + (kt % kStages) * kStage;
-        const uint16_t *sa = sw + kTileN * kTileK;
-        const uint32_t c = 2u * ks + fhalf;
-        fw[b] = *reinterpret_cast<const u32x4 *>(sw + lds_at(wn * kWaveSpan + b * 32 + frow, c));
-        fa[b] = *reinterpret_cast<const u32x4 *>(sa + lds_at(wt * kWaveSpan + b * 32 + frow, c));
-    };
-    auto frags = [&](int kt, int ks, u32x4 (&fw)[kBlk], u32x4 (&fa)[kBlk]) {
-#pragma unroll
-        for (int b = 0; b < kBlk; ++b) frag_part(kt, ks, b, fw, fa);
+    auto frag_part = [&](const LaneOffs &lo, int kt, int ks, int b, u32x4 (&fw)[kBlk],
+                         u32x4 (&fa)[kBlk]) {
+        const uint32_t off = ((ks ? lo.cx1 : lo.cx0) ^ ((uint32_t)(kt & 1) << 6)) +
+                             (uint32_t)b * (32 * kPairK * 2);
+        const uint32_t pb = (uint32_t)((kt >> 1) & 1);
+        fw[b] = *reinterpret_cast<const u32x4 *>(lbytes + lo.fbw + off + pb * (kPair * 2));
+        fa[b] = *reinterpret_cast<const u32x4 *>(lbytes + lo.fba + off + pb * (kPair * 2));
     };
 
     Tile cur;
     if (!tile_at(0, cur)) return;
-    prologue_issue(cur);
+    pair_in(cur, 0);
+    if (KP > 1) pair_in(cur, 1);
     for (int it = 0;; ++it) {
         f32x16 acc[kBlk][kBlk];
 #pragma unroll
@@ -299,16 +331,18 @@ void linear_quantize_kernel(
 #pragma unroll
             for (int b = 0; b < kBlk; ++b) acc[a][b] = f32x16{};
 
-        // One stage = 2 steps of k = 16, 16 MFMAs each, over an LDS ring of
-        // kStages buffers. At stage kt the loads of stage kt + kStages - 1 go
-        // out (into the buffer stage kt - 1 used); step 0's MFMAs overlap the
-        // reads of step 1's fragments; then this wave waits until its loads
-        // of stage kt + 1 have landed (the later stages' loads stay in flight)
-        // and the workgroup barrier publishes stage kt + 1; step 1's MFMAs
-        // overlap the reads of its first fragments. Every read of a buffer
-        // happens before the barrier that precedes its refill. (Loads complete
-        // in order, so these vmcnt bounds hold even with the previous tile's
-        // stores still in flight: those only add younger or older stores.)
+        // One stage = 2 steps of k = 16, 16 MFMAs each; a pair = 2 stages in
+        // one LDS buffer. Pair p + 1 is in flight while pair p is computed:
+        // in the middle of stage 2p + 1 this wave waits for its loads of pair
+        // p + 1 and the workgroup barrier publishes them (every wave has then
+        // also read its last fragments of pair p: fragments are read one step
+        // ahead); the next step's MFMAs overlap the first fragment reads of
+        // pair p + 1 and the issue of pair p + 2 into pair p's buffer. Nothing
+        // else is outstanding at that wait, so it is vmcnt(0). (Loads complete
+        // in order, so these counts hold with the previous tile's stores still
+        // in flight too.) The wait, the barrier and the issue sit behind
+        // uniform branches; the matrix-core work is never under a condition,
+        // which would make the compiler spill the accumulators.
         u32x4 fw[2][kBlk], fa[2][kBlk];
         // A step in four chunks: chunk nb = the 4 MFMAs of W block nb, then
         // `side(nb)` (the LDS reads and staging loads that overlap them);
@@ -324,46 +358,35 @@ void linear_quantize_kernel(
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        // ISSUE: stage kt + kStages - 1 exists; PEND: stages issued after
-        // kt + 1 (0, 1 or 2 -- they may stay in flight); LAST: no stage follows
-        auto stage = [&](int kt, auto issue_tag, auto pend_tag, auto last_tag) {
-            constexpr bool ISSUE = decltype(issue_tag)::value;
-            constexpr int PEND = decltype(pend_tag)::value;
-            constexpr bool LAST = decltype(last_tag)::value;
-            step(0, [&](int nb) {
-                if constexpr (ISSUE) stage_in_part(cur, kt + kStages - 1, nb);
-                frag_part(kt, 1, nb, fw[1], fa[1]);
-            });
-            if constexpr (!LAST) {
-                wait_loads<PEND * kLoadsPerStage>();
-                barrier_keep_loads();
-                step(1, [&](int nb) { frag_part(kt + 1, 0, nb, fw[0], fa[0]); });
-            } else {
-                step(1, [&](int) {});
-            }
-        };
-        using T_ = std::true_type;
-        using F_ = std::false_type;
-        using P0 = std::integral_constant<int, 0>;
-        using P1 = std::integral_constant<int, 1>;
-        using P2 = std::integral_constant<int, 2>;
 
-        // the tile's first stages are in flight: wait for stage 0
-        if (KT > 2) wait_loads<2 * kLoadsPerStage>();
-        else if (KT > 1) wait_loads<kLoadsPerStage>();
+        const LaneOffs lo = lane_offs();
+        // pairs 0 and (when there is one) 1 are in flight: wait for pair 0
+        if (KP > 1) wait_loads<kLoadsPerPair>();
         else wait_loads<0>();
         barrier_keep_loads();
-        frags(0, 0, fw[0], fa[0]);
-        for (int kt = 0; kt + 3 < KT; ++kt) stage(kt, T_{}, P2{}, F_{});
-        if (KT >= 3) stage(KT - 3, F_{}, P1{}, F_{});
-        if (KT >= 2) stage(KT - 2, F_{}, P0{}, F_{});
-        stage(KT - 1, F_{}, P0{}, T_{});
+#pragma unroll
+        for (int b = 0; b < kBlk; ++b) frag_part(lo, 0, 0, b, fw[0], fa[0]);
+        for (int kt = 0; kt + 1 < KT; ++kt) {
+            step(0, [&](int nb) { frag_part(lo, kt, 1, nb, fw[1], fa[1]); });
+            const bool odd = (kt & 1) != 0;
+            if (odd) {
+                wait_loads<0>();
+                barrier_keep_loads();
+            }
+            const bool issue = odd && (kt >> 1) + 2 < KP;
+            step(1, [&](int nb) {
+                frag_part(lo, kt + 1, 0, nb, fw[0], fa[0]);
+                if (issue) pair_in_part(lo, cur, (kt >> 1) + 2, nb);
+            });
+        }
+        step(0, [&](int nb) { frag_part(lo, KT - 1, 1, nb, fw[1], fa[1]); });
+        step(1, [&](int) {});
 
         __syncthreads();   // every wave has read its last operand fragments
         Tile nxt;
         const bool more = tile_at(it + 1, nxt);
         if constexpr (kEarly) {
-            if (more) prologue_issue(nxt);
+            if (more) pair_in(nxt, 0);
         }
 
         // ---- epilogue: round to the dtype, quantize per (token, group) ----
@@ -377,6 +400,7 @@ void linear_quantize_kernel(
         uint8_t *lc = reinterpret_cast<uint8_t *>(lds) + kStagingOff;
         uint8_t *lsz = lc + kTileT * kCodePitch;         // s rows, then z rows
         const int Hg = H / G;
+        const uint32_t frow = (uint32_t)lane & 31u, fhalf = (uint32_t)lane >> 5;
         const uint32_t h4 = 4u * fhalf;
         const uint32_t lane_y = frow * (uint32_t)H * 2u;
         const int r = cur.r, n0 = cur.n0, t0 = cur.t0;
@@ -432,46 +456,53 @@ void linear_quantize_kernel(
                     *reinterpret_cast<uint16_t *>(lsz + kTileT * kMetaRow + m) = p.z16;
                 }
             }
+            // one token block at a time: interleaving all of them would need
+            // more registers than there are
+            __builtin_amdgcn_sched_barrier(0);
         }
         // this wave's LDS writes are done (the next tile's staging loads may
         // stay in flight), then every wave's
         wait_loads<63>();
         barrier_keep_loads();
 
-        // write-out of the tile's live token rows
+        // write-out of the tile's live token rows. The thread's offsets are
+        // recomputed for every tile from a fresh copy of its id: hoisted out
+        // of the tile loop they would all stay live across the main loop.
+        const uint32_t wtid = fresh(tid);
         const int rows = min(kTileT, T - t0);
         const size_t grow0 = (size_t)r * T + (size_t)t0;
-        uint8_t *cg = codes + (grow0 * (size_t)H + (size_t)n0) * BITS / 8;
+        FC_GLOBAL uint8_t *cg = sgpr_ptr(codes + (grow0 * (size_t)H + (size_t)n0) * BITS / 8);
         const uint32_t cpitch = (uint32_t)H * BITS / 8;
         constexpr int kCodeChunks = kCodeRow / 16;
     #pragma unroll
         for (int i = 0; i < kTileT * kCodeChunks / kBlockThreads; ++i) {
-            const uint32_t id = (uint32_t)i * kBlockThreads + tid;
+            const uint32_t id = (uint32_t)i * kBlockThreads + wtid;
             const uint32_t row = id / kCodeChunks, c = id % kCodeChunks;
             if ((int)row < rows)
-                stv<u32x4, false>(cg, row * cpitch + c * 16u,
-                                  *reinterpret_cast<const u32x4 *>(lc + row * kCodePitch + c * 16u));
+                stg<u32x4>(cg, row * cpitch + c * 16u,
+                           *reinterpret_cast<const u32x4 *>(lc + row * kCodePitch + c * 16u));
         }
-        uint16_t *sg = s + grow0 * (size_t)Hg + (size_t)(n0 / G);
-        uint16_t *zg = z + grow0 * (size_t)Hg + (size_t)(n0 / G);
+        FC_GLOBAL uint16_t *sg = sgpr_ptr(s + grow0 * (size_t)Hg + (size_t)(n0 / G));
+        FC_GLOBAL uint16_t *zg = sgpr_ptr(z + grow0 * (size_t)Hg + (size_t)(n0 / G));
         const uint32_t mpitch = (uint32_t)Hg * 2u;
         constexpr int kMetaWords = kMetaRow / 4;         // 4-byte pieces of a row
     #pragma unroll
         for (int i = 0; i < (kTileT * kMetaWords + kBlockThreads - 1) / kBlockThreads; ++i) {
-            const uint32_t id = (uint32_t)i * kBlockThreads + tid;
+            const uint32_t id = (uint32_t)i * kBlockThreads + wtid;
             const uint32_t row = id / kMetaWords, c = id % kMetaWords;
             if ((int)row < rows) {
                 const uint32_t at = row * kMetaRow + c * 4u;
-                stv<uint32_t, false>(sg, row * mpitch + c * 4u, *reinterpret_cast<const uint32_t *>(lsz + at));
-                stv<uint32_t, false>(zg, row * mpitch + c * 4u,
-                                     *reinterpret_cast<const uint32_t *>(lsz + kTileT * kMetaRow + at));
+                stg<uint32_t>(sg, row * mpitch + c * 4u, *reinterpret_cast<const uint32_t *>(lsz + at));
+                stg<uint32_t>(zg, row * mpitch + c * 4u,
+                              *reinterpret_cast<const uint32_t *>(lsz + kTileT * kMetaRow + at));
             }
         }
 
         wait_loads<63>();   // the staging area has been read out by every wave
         barrier_keep_loads();
         if (!more) break;
-        if constexpr (!kEarly) prologue_issue(nxt);
+        if constexpr (!kEarly) pair_in(nxt, 0);
+        if (KP > 1) pair_in(nxt, 1);
         cur = nxt;
     }
 }
