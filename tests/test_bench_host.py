@@ -52,3 +52,16 @@ def test_more_than_one_gpu_refused():
     assert p.returncode == 2
     msg = json.loads(p.stdout.strip().splitlines()[-1])
     assert msg["n_gpus"] == 2 and "single GPU" in msg["error"]
+
+
+def test_k1_event_sampling_stride():
+    """K1 is bracketed by events on every 10th timed step, keeping at least 20
+    samples when the run allows it, and every step of a short run."""
+    assert bench.k1_sample_every(200) == 10
+    assert bench.k1_sample_every(1000) == 10
+    assert bench.k1_sample_every(100) == 5
+    assert bench.k1_sample_every(20) == 1
+    assert bench.k1_sample_every(5) == 1
+    for k in (1, 7, 40, 199, 200, 5000):
+        every = bench.k1_sample_every(k)
+        assert len(range(0, k, every)) >= min(k, 20)
