@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfc.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["fc_api.hip", "fc_quantize.hip", "fc_dequant_sum_requant.hip", "fc_dequantize.hip",
-           "fc_sum.hip", "fc_linear_quantize.hip"]
+           "fc_sum.hip", "fc_linear_quantize.hip", "fc_allreduce_small.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -1,0 +1,178 @@
+// The whole emulated all-reduce of "Flash Communication: Reducing Tensor
+// Parallelization Bottleneck for Fast Large Language Model Inference"
+// (Figure 5, right: quantize, Reduce-Scatter reduction and requantize,
+// All-Gather dequantize) in ONE launch, for shapes where launching the three
+// stage kernels one after the other costs more than their memory traffic
+// (decode-sized calls: 14.5 MB moved, under 2 us at HBM speed).
+//
+// Every output position depends only on the same position of the R operands,
+// within whole quantization groups. So a wave can take a run of positions
+// through all three stages alone: quantize each operand's values, dequantize
+// those codes and sum them, requantize the sums, dequantize those. The
+// arithmetic is that of the three stage kernels, step for step (the same
+// device helpers), and both payloads are written to the caller's workspace as
+// the three-launch path writes them -- they are the hand-offs the real
+// exchange would carry -- but each stage takes its input from the registers
+// of the previous one instead of reading the payload back.
+//
+// Work layout: a wave owns one slot of 512 consecutive positions, a lane 8 of
+// them (one 16-byte load per operand); a group of G <= 512 positions covers
+// G/8 lanes. Used when the stage-1 and stage-2 groups are equal (group <= H/R)
+// and R <= 8.
+#include "fc_device.h"
+#include "fc_launch.h"
+
+namespace fc {
+namespace {
+
+constexpr int kMaxR = 8;
+
+// lanes_minmax over aligned groups of L lanes, L given at run time (uniform)
+__device__ __forceinline__ void lanes_minmax_any(float &mn, float &mx, int L) {
+    switch (L) {
+    case 2: lanes_minmax<2>(mn, mx); break;
+    case 4: lanes_minmax<4>(mn, mx); break;
+    case 8: lanes_minmax<8>(mn, mx); break;
+    case 16: lanes_minmax<16>(mn, mx); break;
+    case 32: lanes_minmax<32>(mn, mx); break;
+    case 64: lanes_minmax<64>(mn, mx); break;
+    default: break;   // 1 lane: nothing to combine
+    }
+}
+
+// `res` and `out` may be the same array: every lane reads its residual
+// values before it writes its outputs.
+template <int DT, int BITS1, int BITS2, bool RES>
+__global__ __launch_bounds__(kBlockThreads) void allreduce_small_kernel(
+    const uint16_t *__restrict__ x, int R, uint64_t n, int g_shift, uint8_t *__restrict__ codes1,
+    uint16_t *__restrict__ s1, uint16_t *__restrict__ z1, uint8_t *__restrict__ codes2,
+    uint16_t *__restrict__ s2, uint16_t *__restrict__ z2, const uint16_t *res, uint16_t *out) {
+    constexpr int W1 = BITS1 == 4 ? 1 : 2, W2 = BITS2 == 4 ? 1 : 2;
+    const int lane = lane_id();
+    const uint64_t tile = wave_index() * (uint64_t)kSlotElems;
+    if (tile >= n) return;
+    const uint64_t left = n - tile;
+    const uint32_t avail = left < (uint64_t)kSlotElems ? (uint32_t)left : (uint32_t)kSlotElems;
+    const int L = (1 << g_shift) / kLaneElems;            // lanes per group
+    // n is a multiple of the group and the slot holds whole groups, so a
+    // group's lanes are all inside the data or all past its end. Lanes past
+    // the end (last slot only) load the slot's first positions instead: every
+    // load is unconditional; their groups are their own and nothing of them
+    // is stored.
+    const uint32_t rel = (uint32_t)lane * kLaneElems;
+    const bool valid = rel < avail;
+    const uint32_t lrel = valid ? rel : 0u;
+    const bool leader = valid && (lane & (L - 1)) == 0;    // stores the group's scale and zero
+    const uint64_t gpos = (tile + rel) >> g_shift;         // group of the lane's positions
+
+    // all operands' values (and the residual) in flight together
+    u32x4 raw[kMaxR];
+#pragma unroll
+    for (int r = 0; r < kMaxR; ++r)
+        if (r < R) raw[r] = ldv<u32x4, true>(x + (uint64_t)r * n + tile, lrel * 2);
+    u32x4 rv = {};
+    if constexpr (RES) rv = ldv<u32x4, true>(res + tile, lrel * 2);
+
+    // stage 1 per operand (the quantizer), then its dequantized codes summed
+    // in ascending r starting from operand 0
+    float y[kLaneElems];
+#pragma unroll
+    for (int r = 0; r < kMaxR; ++r) {
+        if (r >= R) break;
+        float v[kLaneElems], mn, mx;
+        widen8<DT>(raw[r], v);
+        minmax8(v, mn, mx);
+        lanes_minmax_any(mn, mx, L);
+        const GroupParams p = group_params<BITS1>(mn, mx);
+        uint32_t w[W1];
+        encode8<BITS1>(v, p, w);
+        const uint64_t e0 = (uint64_t)r * n + tile;
+        if (valid) store_codes<BITS1, false>(codes1 + e0 * BITS1 / 8, rel, w);
+        if (leader) {
+            const uint64_t g = (uint64_t)r * (n >> g_shift) + gpos;
+            s1[g] = p.s16;
+            z1[g] = p.z16;
+        }
+        float xh[kLaneElems];
+        dequant8<BITS1>(w, p.s16, p.z16, xh);
+#pragma unroll
+        for (int k = 0; k < kLaneElems; ++k) y[k] = r == 0 ? xh[k] : y[k] + xh[k];
+    }
+
+    // stage 2: the sums requantized
+    float mn, mx;
+    minmax8(y, mn, mx);
+    lanes_minmax_any(mn, mx, L);
+    const GroupParams p2 = group_params<BITS2>(mn, mx);
+    uint32_t w2[W2];
+    encode8<BITS2>(y, p2, w2);
+    if (valid) store_codes<BITS2, false>(codes2 + tile * BITS2 / 8, rel, w2);
+    if (leader) {
+        s2[gpos] = p2.s16;
+        z2[gpos] = p2.z16;
+    }
+
+    // the final dequantize (and the residual add)
+    float o[kLaneElems];
+    dequant8<BITS2>(w2, p2.s16, p2.z16, o);
+    u32x4 packed = narrow8<DT>(o);
+    if constexpr (RES) {
+        float a[kLaneElems], rr[kLaneElems];
+        widen8<DT>(packed, a);   // the all-reduce result as the dtype holds it
+        widen8<DT>(rv, rr);
+#pragma unroll
+        for (int k = 0; k < kLaneElems; ++k) a[k] = rr[k] + a[k];
+        packed = narrow8<DT>(a);
+    }
+    if (valid) stv<u32x4, true>(out + tile, rel * 2, packed);
+}
+
+template <int DT, int BITS1, int BITS2, bool RES>
+hipError_t launch_one(const uint16_t *x, int R, uint64_t n, int g_shift, uint8_t *codes1,
+                      uint16_t *s1, uint16_t *z1, uint8_t *codes2, uint16_t *s2, uint16_t *z2,
+                      const uint16_t *res, uint16_t *out, hipStream_t stream) {
+    constexpr uint64_t per_block = (uint64_t)kWavesPerBlock * kSlotElems;
+    const uint64_t blocks = (n + per_block - 1) / per_block;
+    if (blocks > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((allreduce_small_kernel<DT, BITS1, BITS2, RES>), dim3((unsigned)blocks),
+                       dim3(kBlockThreads), 0, stream, x, R, n, g_shift, codes1, s1, z1, codes2, s2,
+                       z2, res, out);
+    return hipGetLastError();
+}
+
+template <int DT, bool RES>
+hipError_t by_bits(const uint16_t *x, int R, uint64_t n, int bits1, int bits2, int g_shift,
+                   uint8_t *codes1, uint16_t *s1, uint16_t *z1, uint8_t *codes2, uint16_t *s2,
+                   uint16_t *z2, const uint16_t *res, uint16_t *out, hipStream_t stream) {
+#define FC_ARGS x, R, n, g_shift, codes1, s1, z1, codes2, s2, z2, res, out, stream
+    if (bits1 == 4)
+        return bits2 == 4 ? launch_one<DT, 4, 4, RES>(FC_ARGS) : launch_one<DT, 4, 8, RES>(FC_ARGS);
+    return bits2 == 4 ? launch_one<DT, 8, 4, RES>(FC_ARGS) : launch_one<DT, 8, 8, RES>(FC_ARGS);
+#undef FC_ARGS
+}
+
+}  // namespace
+
+bool allreduce_small_applies(int R, uint64_t n, int group, int group2) {
+    return R >= 1 && R <= kMaxR && group == group2 && group >= kLaneElems && group <= kSlotElems &&
+           (uint64_t)R * n <= kAllreduceSmallMaxElems;
+}
+
+hipError_t launch_allreduce_small(const uint16_t *x, int dtype, int R, uint64_t n, int bits1,
+                                  int bits2, int group, uint8_t *codes1, uint16_t *s1,
+                                  uint16_t *z1, uint8_t *codes2, uint16_t *s2, uint16_t *z2,
+                                  const uint16_t *residual, uint16_t *out, hipStream_t stream) {
+    const int sh = ilog2(group);
+    if (residual) {
+        return dtype == 0 ? by_bits<0, true>(x, R, n, bits1, bits2, sh, codes1, s1, z1, codes2, s2,
+                                             z2, residual, out, stream)
+                          : by_bits<1, true>(x, R, n, bits1, bits2, sh, codes1, s1, z1, codes2, s2,
+                                             z2, residual, out, stream);
+    }
+    return dtype == 0 ? by_bits<0, false>(x, R, n, bits1, bits2, sh, codes1, s1, z1, codes2, s2, z2,
+                                          nullptr, out, stream)
+                      : by_bits<1, false>(x, R, n, bits1, bits2, sh, codes1, s1, z1, codes2, s2, z2,
+                                          nullptr, out, stream);
+}
+
+}  // namespace fc

@@ -82,8 +82,9 @@ fc_status check_shape2(int R, int T, int H, int bits1, int bits2, int group, int
     return FC_OK;
 }
 
-// The three launches of the emulated all-reduce; with_residual: the last one
-// adds the result to `residual`.
+// The emulated all-reduce: the three stage launches, or for launch-bound
+// shapes (decode-sized) the single launch that computes the same payloads and
+// output; with_residual: the result is added to `residual`.
 fc_status allreduce_emulated(const void *x, fc_dtype dt, int R, int T, int H, int bits1, int bits2,
                              int group, bool with_residual, const void *residual, void *out,
                              void *workspace, size_t workspace_bytes, void *stream) {
@@ -106,6 +107,11 @@ fc_status allreduce_emulated(const void *x, fc_dtype dt, int R, int T, int H, in
     uint16_t *s2 = reinterpret_cast<uint16_t *>(ws + L.off[4]);
     uint16_t *z2 = reinterpret_cast<uint16_t *>(ws + L.off[5]);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (fc::allreduce_small_applies(R, n, group, g2))
+        return from_hip(fc::launch_allreduce_small(
+            static_cast<const uint16_t *>(x), (int)dt, R, n, bits1, bits2, group, codes1, s1, z1,
+            codes2, s2, z2, with_residual ? static_cast<const uint16_t *>(residual) : nullptr,
+            static_cast<uint16_t *>(out), s));
     st = from_hip(fc::launch_quantize(static_cast<const uint16_t *>(x), (int)dt, n * (uint64_t)R, bits1,
                                       group, codes1, s1, z1, s));
     if (st != FC_OK) return st;

@@ -39,6 +39,18 @@ hipError_t launch_linear_quantize(const uint16_t *a, const uint16_t *w, int dtyp
                                   int K, int H, int bits, int group, uint8_t *codes, uint16_t *s,
                                   uint16_t *z, uint16_t *y, hipStream_t stream);
 
+// The whole emulated all-reduce in one launch, for launch-bound shapes:
+// stage-1 payload (codes1, s1, z1 as launch_quantize writes them), stage-2
+// payload (as launch_dequant_sum_requant writes them) and the output (as
+// launch_dequantize or, with residual != NULL, launch_dequantize_residual
+// writes it), identical bit for bit. Applies when allreduce_small_applies.
+constexpr uint64_t kAllreduceSmallMaxElems = uint64_t(1) << 24;   // R * T * H
+bool allreduce_small_applies(int R, uint64_t n, int group, int group2);
+hipError_t launch_allreduce_small(const uint16_t *x, int dtype, int R, uint64_t n, int bits1,
+                                  int bits2, int group, uint8_t *codes1, uint16_t *s1,
+                                  uint16_t *z1, uint8_t *codes2, uint16_t *s2, uint16_t *z2,
+                                  const uint16_t *residual, uint16_t *out, hipStream_t stream);
+
 // Uncompressed R-way sum over n = T*H positions of R operands laid out [R][n].
 hipError_t launch_sum(const uint16_t *x, int dtype, int R, uint64_t n, uint16_t *out,
                       hipStream_t stream);
