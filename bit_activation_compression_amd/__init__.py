@@ -103,10 +103,19 @@ def _ptr(t: torch.Tensor | None):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# torch's current stream as a raw handle without building a Stream object
+# (a few microseconds per call, which matters for decode-sized calls); the
+# public route where this accessor does not exist
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream, device) -> ctypes.c_void_p:
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream)
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    if _raw_current_stream is not None:
+        idx = device.index if device.index is not None else torch.cuda.current_device()
+        return ctypes.c_void_p(_raw_current_stream(idx))
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
 def _dev_tensor(t: torch.Tensor, name: str) -> None:

@@ -106,6 +106,9 @@ fc_status fc_dequantize(const uint8_t *codes2, const uint16_t *s2, const uint16_
  * The whole emulated all-reduce on one GPU: fc_quantize_groups, then
  * fc_dequant_sum_requant, then fc_dequantize, with both payloads placed in the
  * caller's workspace (layout: fc_workspace_layout). out [T][H] in dt.
+ * Launch-bound calls (R*T*H <= 2^24, R <= 8, group == stage-2 group <= 512)
+ * run as one kernel launch that writes the same payloads and output, bit for
+ * bit; larger ones as the three launches.
  */
 fc_status fc_allreduce_emulated(const void *x, fc_dtype dt, int R, int T, int H, int bits, int group,
                                 void *out, void *workspace, size_t workspace_bytes, void *stream);

@@ -159,3 +159,22 @@ def test_threshold(T):
     x = _operands(R, T, H, synth.BF16, seed=T)
     got = _fused(x, synth.BF16, 4, 4, group)
     _same(got, _oracle(x, synth.BF16, 4, 4, group), f"T={T}")
+
+
+def test_stream_handle_is_torchs_current_stream():
+    """The binding passes torch's current stream (raw handle) to the library,
+    also inside a `torch.cuda.stream` context, and a call made there is ordered
+    on that stream."""
+    from bit_activation_compression_amd import _stream
+    dev = torch.device("cuda", torch.cuda.current_device())
+    assert _stream(None, dev).value == torch.cuda.current_stream(dev).cuda_stream or \
+        (_stream(None, dev).value is None and torch.cuda.current_stream(dev).cuda_stream == 0)
+    side = torch.cuda.Stream()
+    x = _dev(_operands(2, 8, 256, synth.F16, seed=1), synth.F16)
+    ref, _ = fc.fc_allreduce_emulated(x, 8, 128)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        assert _stream(None, dev).value == side.cuda_stream
+        out, _ = fc.fc_allreduce_emulated(x, 8, 128)
+    side.synchronize()
+    assert torch.equal(out, ref)
