@@ -19,6 +19,8 @@
 // them (one 16-byte load per operand); a group of G <= 512 positions covers
 // G/8 lanes. Used when the stage-1 and stage-2 groups are equal (group <= H/R)
 // and R <= 8.
+#include <type_traits>
+
 #include "fc_device.h"
 #include "fc_launch.h"
 
@@ -27,27 +29,41 @@ namespace {
 
 constexpr int kMaxR = 8;
 
-// lanes_minmax over aligned groups of L lanes, L given at run time (uniform)
-__device__ __forceinline__ void lanes_minmax_any(float &mn, float &mx, int L) {
+// lanes_minmax over aligned groups of L lanes (L given at run time, uniform)
+// for the first `count` of N value pairs; one branch for all of them, so the
+// pairs' cross-lane steps interleave
+template <int N>
+__device__ __forceinline__ void lanes_minmax_any(float (&mn)[N], float (&mx)[N], int count, int L) {
+    auto all = [&](auto l_tag) {
+        constexpr int LL = decltype(l_tag)::value;
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if (i < count) lanes_minmax<LL>(mn[i], mx[i]);
+    };
     switch (L) {
-    case 2: lanes_minmax<2>(mn, mx); break;
-    case 4: lanes_minmax<4>(mn, mx); break;
-    case 8: lanes_minmax<8>(mn, mx); break;
-    case 16: lanes_minmax<16>(mn, mx); break;
-    case 32: lanes_minmax<32>(mn, mx); break;
-    case 64: lanes_minmax<64>(mn, mx); break;
+    case 2: all(std::integral_constant<int, 2>{}); break;
+    case 4: all(std::integral_constant<int, 4>{}); break;
+    case 8: all(std::integral_constant<int, 8>{}); break;
+    case 16: all(std::integral_constant<int, 16>{}); break;
+    case 32: all(std::integral_constant<int, 32>{}); break;
+    case 64: all(std::integral_constant<int, 64>{}); break;
     default: break;   // 1 lane: nothing to combine
     }
 }
 
 // `res` and `out` may be the same array: every lane reads its residual
-// values before it writes its outputs.
-template <int DT, int BITS1, int BITS2, bool RES>
+// values before it writes its outputs. RT > 0: the operand count is a
+// compile-time constant, so the operands' independent chains (group min/max,
+// scale, reciprocal, codes) interleave -- a decode call has one wave per
+// SIMD, and nothing else hides their latency; RT == 0: any R <= 8.
+template <int DT, int BITS1, int BITS2, bool RES, int RT>
 __global__ __launch_bounds__(kBlockThreads) void allreduce_small_kernel(
-    const uint16_t *__restrict__ x, int R, uint64_t n, int g_shift, uint8_t *__restrict__ codes1,
+    const uint16_t *__restrict__ x, int R_arg, uint64_t n, int g_shift, uint8_t *__restrict__ codes1,
     uint16_t *__restrict__ s1, uint16_t *__restrict__ z1, uint8_t *__restrict__ codes2,
     uint16_t *__restrict__ s2, uint16_t *__restrict__ z2, const uint16_t *res, uint16_t *out) {
     constexpr int W1 = BITS1 == 4 ? 1 : 2, W2 = BITS2 == 4 ? 1 : 2;
+    constexpr int NR = RT > 0 ? RT : kMaxR;              // operand slots
+    const int R = RT > 0 ? RT : R_arg;
     const int lane = lane_id();
     const uint64_t tile = wave_index() * (uint64_t)kSlotElems;
     if (tile >= n) return;
@@ -66,24 +82,31 @@ __global__ __launch_bounds__(kBlockThreads) void allreduce_small_kernel(
     const uint64_t gpos = (tile + rel) >> g_shift;         // group of the lane's positions
 
     // all operands' values (and the residual) in flight together
-    u32x4 raw[kMaxR];
+    u32x4 raw[NR];
 #pragma unroll
-    for (int r = 0; r < kMaxR; ++r)
-        if (r < R) raw[r] = ldv<u32x4, true>(x + (uint64_t)r * n + tile, lrel * 2);
+    for (int r = 0; r < NR; ++r)
+        if (RT > 0 || r < R) raw[r] = ldv<u32x4, true>(x + (uint64_t)r * n + tile, lrel * 2);
     u32x4 rv = {};
     if constexpr (RES) rv = ldv<u32x4, true>(res + tile, lrel * 2);
 
     // stage 1 per operand (the quantizer), then its dequantized codes summed
-    // in ascending r starting from operand 0
+    // in ascending r starting from operand 0. The operands go through each
+    // phase together (group minima and maxima, their cross-lane steps, then
+    // codes and sums), so their independent chains interleave.
+    float v1[NR][kLaneElems], mn1[NR], mx1[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        if (RT == 0 && r >= R) break;
+        widen8<DT>(raw[r], v1[r]);
+        minmax8(v1[r], mn1[r], mx1[r]);
+    }
+    lanes_minmax_any<NR>(mn1, mx1, R, L);
     float y[kLaneElems];
 #pragma unroll
-    for (int r = 0; r < kMaxR; ++r) {
-        if (r >= R) break;
-        float v[kLaneElems], mn, mx;
-        widen8<DT>(raw[r], v);
-        minmax8(v, mn, mx);
-        lanes_minmax_any(mn, mx, L);
-        const GroupParams p = group_params<BITS1>(mn, mx);
+    for (int r = 0; r < NR; ++r) {
+        if (RT == 0 && r >= R) break;
+        const float (&v)[kLaneElems] = v1[r];
+        const GroupParams p = group_params<BITS1>(mn1[r], mx1[r]);
         uint32_t w[W1];
         encode8<BITS1>(v, p, w);
         const uint64_t e0 = (uint64_t)r * n + tile;
@@ -100,10 +123,10 @@ __global__ __launch_bounds__(kBlockThreads) void allreduce_small_kernel(
     }
 
     // stage 2: the sums requantized
-    float mn, mx;
-    minmax8(y, mn, mx);
-    lanes_minmax_any(mn, mx, L);
-    const GroupParams p2 = group_params<BITS2>(mn, mx);
+    float mn[1], mx[1];
+    minmax8(y, mn[0], mx[0]);
+    lanes_minmax_any<1>(mn, mx, 1, L);
+    const GroupParams p2 = group_params<BITS2>(mn[0], mx[0]);
     uint32_t w2[W2];
     encode8<BITS2>(y, p2, w2);
     if (valid) store_codes<BITS2, false>(codes2 + tile * BITS2 / 8, rel, w2);
@@ -127,17 +150,31 @@ __global__ __launch_bounds__(kBlockThreads) void allreduce_small_kernel(
     if (valid) stv<u32x4, true>(out + tile, rel * 2, packed);
 }
 
+template <int DT, int BITS1, int BITS2, bool RES, int RT>
+hipError_t launch_rt(const uint16_t *x, int R, uint64_t n, int g_shift, uint8_t *codes1,
+                     uint16_t *s1, uint16_t *z1, uint8_t *codes2, uint16_t *s2, uint16_t *z2,
+                     const uint16_t *res, uint16_t *out, hipStream_t stream) {
+    constexpr uint64_t per_block = (uint64_t)kWavesPerBlock * kSlotElems;
+    const uint64_t blocks = (n + per_block - 1) / per_block;
+    if (blocks > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((allreduce_small_kernel<DT, BITS1, BITS2, RES, RT>), dim3((unsigned)blocks),
+                       dim3(kBlockThreads), 0, stream, x, R, n, g_shift, codes1, s1, z1, codes2, s2,
+                       z2, res, out);
+    return hipGetLastError();
+}
+
 template <int DT, int BITS1, int BITS2, bool RES>
 hipError_t launch_one(const uint16_t *x, int R, uint64_t n, int g_shift, uint8_t *codes1,
                       uint16_t *s1, uint16_t *z1, uint8_t *codes2, uint16_t *s2, uint16_t *z2,
                       const uint16_t *res, uint16_t *out, hipStream_t stream) {
-    constexpr uint64_t per_block = (uint64_t)kWavesPerBlock * kSlotElems;
-    const uint64_t blocks = (n + per_block - 1) / per_block;
-    if (blocks > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((allreduce_small_kernel<DT, BITS1, BITS2, RES>), dim3((unsigned)blocks),
-                       dim3(kBlockThreads), 0, stream, x, R, n, g_shift, codes1, s1, z1, codes2, s2,
-                       z2, res, out);
-    return hipGetLastError();
+#define FC_ARGS x, R, n, g_shift, codes1, s1, z1, codes2, s2, z2, res, out, stream
+    switch (R) {
+    case 8: return launch_rt<DT, BITS1, BITS2, RES, 8>(FC_ARGS);
+    case 4: return launch_rt<DT, BITS1, BITS2, RES, 4>(FC_ARGS);
+    case 2: return launch_rt<DT, BITS1, BITS2, RES, 2>(FC_ARGS);
+    default: return launch_rt<DT, BITS1, BITS2, RES, 0>(FC_ARGS);
+    }
+#undef FC_ARGS
 }
 
 template <int DT, bool RES>
