@@ -74,11 +74,22 @@ def k1_sample_every(steps: int) -> int:
     return max(1, min(K1_SAMPLE_EVERY, steps // 20))
 
 
+def code_only(src: str) -> str:
+    """C/C++ source without comments and with whitespace runs collapsed: what a
+    comment edit leaves unchanged. (The kernel sources hold no string literals
+    that contain comment markers.)"""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def k1_source_hash() -> str:
+    """Hash of K1's code (comments and layout ignored): the counter summary is
+    valid while the code it was measured on is unchanged."""
     h = hashlib.sha256()
     for rel in K1_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,14 +1,16 @@
 // Device helpers shared by the codec kernels (gfx950, wave64).
 //
-// Work layout common to all kernels: a wave owns a tile of U "slots"; a slot
-// is 64 lanes x 8 consecutive elements = 512 consecutive elements, so every
-// lane reads one 16-byte vector of 16-bit values (or the matching 4- or
-// 8-byte run of codes) per slot and a wave touches 1 KiB of contiguous
-// activations per slot. A quantization group of G elements (a power of two,
-// 8 <= G <= 8192) covers G/8 consecutive lanes of one slot when G <= 512, or
-// G/512 consecutive slots of one wave when G > 512; group minima and maxima
-// are reduced first inside the lane, then across lanes with DPP row
-// operations (<= 16 lanes), ds_swizzle (32 lanes) and readlane (64 lanes).
+// Work layout of the quantize, dequantize and single-launch kernels (the
+// dequant-sum-requant kernel uses runs of 32 elements per lane instead): a
+// wave owns a tile of U "slots"; a slot is 64 lanes x 8 consecutive elements
+// = 512 consecutive elements, so every lane reads one 16-byte vector of
+// 16-bit values (or the matching 4- or 8-byte run of codes) per slot and a
+// wave touches 1 KiB of contiguous activations per slot. A quantization group
+// of G elements (a power of two, 8 <= G <= 8192) covers G/8 consecutive lanes
+// of one slot when G <= 512, or G/512 consecutive slots of one wave when
+// G > 512; group minima and maxima are reduced first inside the lane, then
+// across lanes with DPP row operations (<= 16 lanes), ds_swizzle (32 lanes)
+// and readlane (64 lanes).
 //
 // Addresses are a wave-uniform base (SGPRs) plus a 32-bit per-lane offset,
 // so no lane does 64-bit address arithmetic.

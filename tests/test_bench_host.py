@@ -65,3 +65,10 @@ def test_k1_event_sampling_stride():
     for k in (1, 7, 40, 199, 200, 5000):
         every = bench.k1_sample_every(k)
         assert len(range(0, k, every)) >= min(k, 20)
+
+
+def test_k1_hash_ignores_comments_but_not_code():
+    src = "int a = 1; // one\n/* block\n comment */ int b = a + 2;\n"
+    assert bench.code_only(src) == "int a = 1; int b = a + 2;"
+    assert bench.code_only(src.replace("// one", "// a different note")) == bench.code_only(src)
+    assert bench.code_only(src.replace("a + 2", "a + 3")) != bench.code_only(src)
