@@ -33,6 +33,20 @@ def test_library_exports_every_declared_function():
     assert sorted(names) == sorted(fc.EXPORTED_SYMBOLS)
 
 
+def test_no_kernel_launch_stub_left_undefined():
+    """Every kernel's host-side launch stub is defined in the library (the
+    host compiler pass can drop one silently; loading would then fail)."""
+    import shutil
+    import subprocess
+    from bit_activation_compression_amd import build as libbuild
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    r = subprocess.run([nm, "-D", "--undefined-only", libbuild.LIB], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert "__device_stub__" not in r.stdout
+
+
 def test_status_strings():
     for s in range(8):
         assert fc.fc_status_string(s).startswith("FC_")
