@@ -10,10 +10,10 @@
 // through all three stages alone: quantize each operand's values, dequantize
 // those codes and sum them, requantize the sums, dequantize those. The
 // arithmetic is that of the three stage kernels, step for step (the same
-// device helpers), and both payloads are written to the caller's workspace as
-// the three-launch path writes them -- they are the hand-offs the real
-// exchange would carry -- but each stage takes its input from the registers
-// of the previous one instead of reading the payload back.
+// device helpers), and the stage boundaries go through memory as in the
+// three-launch path: each stage writes its payload to the caller's workspace
+// (the hand-off the real exchange would carry) and the next stage reads it
+// back from there.
 //
 // Work layout: a wave owns one slot of 512 consecutive positions, a lane 8 of
 // them (one 16-byte load per operand); a group of G <= 512 positions covers
@@ -49,6 +49,17 @@ __device__ __forceinline__ void lanes_minmax_any(float (&mn)[N], float (&mx)[N],
     case 64: all(std::integral_constant<int, 64>{}); break;
     default: break;   // 1 lane: nothing to combine
     }
+}
+
+// A stage boundary inside the kernel: this wave's stores of a payload are
+// complete and the payload is then read back from memory (release, then
+// acquire, at device scope: the stores reach L2, the vector L1 is
+// invalidated). Each wave reads back only what it wrote itself -- every
+// position depends only on the same position of the operands -- so no other
+// wave's progress is involved.
+__device__ __forceinline__ void handoff() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
 // `res` and `out` may be the same array: every lane reads its residual
@@ -89,10 +100,10 @@ __global__ __launch_bounds__(kBlockThreads) void allreduce_small_kernel(
     u32x4 rv = {};
     if constexpr (RES) rv = ldv<u32x4, true>(res + tile, lrel * 2);
 
-    // stage 1 per operand (the quantizer), then its dequantized codes summed
-    // in ascending r starting from operand 0. The operands go through each
-    // phase together (group minima and maxima, their cross-lane steps, then
-    // codes and sums), so their independent chains interleave.
+    // ---- stage 1: every operand quantized, payload 1 written ----
+    // The operands go through each phase together (group minima and maxima,
+    // their cross-lane steps, then codes), so their independent chains
+    // interleave.
     float v1[NR][kLaneElems], mn1[NR], mx1[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -101,14 +112,12 @@ __global__ __launch_bounds__(kBlockThreads) void allreduce_small_kernel(
         minmax8(v1[r], mn1[r], mx1[r]);
     }
     lanes_minmax_any<NR>(mn1, mx1, R, L);
-    float y[kLaneElems];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         if (RT == 0 && r >= R) break;
-        const float (&v)[kLaneElems] = v1[r];
         const GroupParams p = group_params<BITS1>(mn1[r], mx1[r]);
         uint32_t w[W1];
-        encode8<BITS1>(v, p, w);
+        encode8<BITS1>(v1[r], p, w);
         const uint64_t e0 = (uint64_t)r * n + tile;
         if (valid) store_codes<BITS1, false>(codes1 + e0 * BITS1 / 8, rel, w);
         if (leader) {
@@ -116,13 +125,40 @@ __global__ __launch_bounds__(kBlockThreads) void allreduce_small_kernel(
             s1[g] = p.s16;
             z1[g] = p.z16;
         }
+    }
+
+    // ---- stage 2: payload 1 read back, dequantized and summed in ascending
+    // r from operand 0, requantized; payload 2 written ----
+    handoff();
+    const uint64_t gl = (tile + lrel) >> g_shift;          // group of the positions this lane reads
+    uint32_t w1[NR][W1];
+    uint16_t sv[NR], zv[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        if (RT == 0 && r >= R) break;
+        const uint64_t e0 = (uint64_t)r * n + tile;
+        const FC_GLOBAL uint8_t *cb = sgpr_ptr(codes1 + e0 * BITS1 / 8);
+        const FC_GLOBAL uint16_t *sb = sgpr_ptr(s1 + (uint64_t)r * (n >> g_shift));
+        const FC_GLOBAL uint16_t *zb = sgpr_ptr(z1 + (uint64_t)r * (n >> g_shift));
+        if constexpr (BITS1 == 4) {
+            w1[r][0] = ldg<uint32_t>(cb, lrel / 2);
+        } else {
+            const u32x2 c = ldg<u32x2>(cb, lrel);
+            w1[r][0] = c.x;
+            w1[r][W1 - 1] = c.y;
+        }
+        sv[r] = ldg<uint16_t>(sb, (uint32_t)gl * 2u);
+        zv[r] = ldg<uint16_t>(zb, (uint32_t)gl * 2u);
+    }
+    float y[kLaneElems];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        if (RT == 0 && r >= R) break;
         float xh[kLaneElems];
-        dequant8<BITS1>(w, p.s16, p.z16, xh);
+        dequant8<BITS1>(w1[r], sv[r], zv[r], xh);
 #pragma unroll
         for (int k = 0; k < kLaneElems; ++k) y[k] = r == 0 ? xh[k] : y[k] + xh[k];
     }
-
-    // stage 2: the sums requantized
     float mn[1], mx[1];
     minmax8(y, mn[0], mx[0]);
     lanes_minmax_any<1>(mn, mx, 1, L);
@@ -135,9 +171,24 @@ __global__ __launch_bounds__(kBlockThreads) void allreduce_small_kernel(
         z2[gpos] = p2.z16;
     }
 
-    // the final dequantize (and the residual add)
+    // ---- stage 3: payload 2 read back and dequantized (and the residual
+    // added); the output written ----
+    handoff();
+    uint32_t w3[W2];
+    {
+        const FC_GLOBAL uint8_t *cb = sgpr_ptr(codes2 + tile * BITS2 / 8);
+        if constexpr (BITS2 == 4) {
+            w3[0] = ldg<uint32_t>(cb, lrel / 2);
+        } else {
+            const u32x2 c = ldg<u32x2>(cb, lrel);
+            w3[0] = c.x;
+            w3[W2 - 1] = c.y;
+        }
+    }
+    const uint16_t s3 = ldg<uint16_t>(sgpr_ptr(s2), (uint32_t)gl * 2u);
+    const uint16_t z3 = ldg<uint16_t>(sgpr_ptr(z2), (uint32_t)gl * 2u);
     float o[kLaneElems];
-    dequant8<BITS2>(w2, p2.s16, p2.z16, o);
+    dequant8<BITS2>(w3, s3, z3, o);
     u32x4 packed = narrow8<DT>(o);
     if constexpr (RES) {
         float a[kLaneElems], rr[kLaneElems];
