@@ -8,7 +8,7 @@ rounding without changing the source:
   - v_fma_mix{lo,hi}_f16 / v_mad_mix{lo,hi}_f16: an fma fused with the
     following fp32 -> fp16 conversion rounds once instead of twice;
   - v_cvt_pkrtz_f16_f32: rounds toward zero;
-  - v_pk_{fma,mul,add}_f32: packed fp32 forms this build keeps out;
+  - v_pk_{fma,mul,add}_f32: packed fp32 forms the build flags keep out;
 and scratch traffic would mean register spills on the hot path.
 This compiles every kernel source to device assembly with the build's own
 flags and checks that none of them appear.
