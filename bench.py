@@ -65,6 +65,7 @@ def link_bytes(R: int, T: int, H: int, bits: int, group: int, group2: int, e: in
 
 
 K1_SAMPLE_EVERY = 10
+GRAPH_CALLS = 20       # calls captured per HIP graph in the launch-bound measurements
 
 
 def k1_sample_every(steps: int) -> int:
@@ -193,25 +194,28 @@ def quality_report(seed: int) -> int:
             total = n1 * 2 + 2 * p1 + 2 * p2 + n2 * 2
             rec.update({"us_per_call": round(ms * 1e3, 2), "gbps": round(total / (ms * 1e-3) / 1e9, 1)})
             if T * H <= 1 << 20:
-                # launch-bound shapes: the same call captured once in a HIP graph and replayed
+                # launch-bound shapes: GRAPH_CALLS consecutive calls captured in one
+                # HIP graph (as a serving step would be) and replayed; per-call time
                 graph = torch.cuda.CUDAGraph()
                 cap = torch.cuda.Stream(dev)
                 cap.wait_stream(stream)
                 with torch.cuda.stream(cap):
                     fc.fc_allreduce_emulated(xd, bits, g, out, ws, stream=cap, bits2=bits2)
                     with torch.cuda.graph(graph, stream=cap):
-                        fc.fc_allreduce_emulated(xd, bits, g, out, ws, stream=cap, bits2=bits2)
+                        for _ in range(GRAPH_CALLS):
+                            fc.fc_allreduce_emulated(xd, bits, g, out, ws, stream=cap, bits2=bits2)
                 stream.wait_stream(cap)
                 torch.cuda.synchronize()
-                for _ in range(5):
+                for _ in range(3):
                     graph.replay()
                 ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
                 ev[0].record(stream)
-                for _ in range(50):
+                for _ in range(10):
                     graph.replay()
                 ev[1].record(stream)
                 torch.cuda.synchronize()
-                rec["us_per_call_graph"] = round(ev[0].elapsed_time(ev[1]) / 50 * 1e3, 2)
+                rec["us_per_call_graph"] = round(ev[0].elapsed_time(ev[1]) / (10 * GRAPH_CALLS) * 1e3, 2)
+                rec["graph_calls_per_replay"] = GRAPH_CALLS
                 del graph
             records.append(rec)
             print(f"[quality] {name} int{bits}->int{bits2}: stage1 {rec['stage1_mse']:.4g} "
