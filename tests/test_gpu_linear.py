@@ -106,6 +106,37 @@ def test_dyadic_inputs_bit_exact(R, T, K, H, group, bits, dtype):
         assert np.array_equal(got2[k], ref[k]), k
 
 
+def _draw_linear(rng):
+    """A supported (R, T, K, H, group, bits, dtype): K a multiple of 32 (odd
+    stage counts included: the last staged pair is then half used), H a
+    multiple of 256 and of R, group <= 128; sizes kept small."""
+    R = int(rng.integers(1, 5))
+    K = 32 * int(rng.integers(1, 24))
+    H = 256 * int(rng.integers(1, 5))
+    if H % R:
+        H *= R                                   # H % R == 0 (the chunking needs it)
+    T = int(rng.integers(1, 600))
+    group = int(2 ** rng.integers(3, 8))
+    bits = int(rng.choice([4, 8]))
+    dtype = oracle.F16 if rng.random() < 0.5 else oracle.BF16
+    return R, T, K, H, group, bits, dtype
+
+
+RANDOM = [_draw_linear(np.random.default_rng(77 + i)) for i in range(16)]
+
+
+@pytest.mark.parametrize("R,T,K,H,group,bits,dtype", RANDOM)
+def test_random_dyadic_shapes(R, T, K, H, group, bits, dtype):
+    _say(f"linear_quantize random R={R} T={T} K={K} H={H} g{group} int{bits} {dtype}")
+    rng = np.random.default_rng(R * T + K * 3 + H)
+    a, w = _dyadic(rng, R, T, K, H, dtype)
+    ref = oracle.linear_quantize(a, w, dtype, bits, group)
+    got = _run(a, w, dtype, bits, group)
+    assert np.array_equal(got["y"], ref["y"])
+    for k in ("codes1", "s1", "z1"):
+        assert np.array_equal(got[k], ref[k]), k
+
+
 def _ulp(v: np.ndarray, dtype: str) -> np.ndarray:
     """Spacing of the dtype at |v| (normal range)."""
     p = 11 if dtype == oracle.F16 else 8
