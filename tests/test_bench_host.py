@@ -72,3 +72,10 @@ def test_k1_hash_ignores_comments_but_not_code():
     assert bench.code_only(src) == "int a = 1; int b = a + 2;"
     assert bench.code_only(src.replace("// one", "// a different note")) == bench.code_only(src)
     assert bench.code_only(src.replace("a + 2", "a + 3")) != bench.code_only(src)
+
+
+def test_k1_counter_summary_is_for_the_current_code():
+    """The committed HBM-counter summary was measured on K1's current code (so
+    bench.py reports roofline.traffic); a change to K1's code needs a new
+    counter run."""
+    assert bench.measured_traffic("llama3_70b_prefill") is not None
