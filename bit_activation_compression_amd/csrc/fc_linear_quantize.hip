@@ -15,9 +15,10 @@
 // those the separate stage-1 quantizer gives for that stored y_r.
 //
 // Work layout (gfx950, wave64, v_mfma_f32_32x32x16_{bf16,f16}):
-//   - a workgroup of 4 waves owns a 256 (channels n) x 256 (tokens t) output
-//     tile of one rank; wave (wn, wt) owns 128 x 128 of it as 4 x 4 MFMA
-//     blocks of 32 x 32;
+//   - a workgroup of 8 waves (2 per SIMD, so that one wave's matrix-core work
+//     covers the other's waits) owns a 256 (channels n) x 256 (tokens t)
+//     output tile of one rank; wave (wn, wt) owns 128 x 64 of it as 4 x 2
+//     MFMA blocks of 32 x 32;
 //   - the MFMA's row operand is W (rows n) and its column operand is A (rows
 //     t), so the accumulator of a lane holds, for ONE token t (lane % 32), 16
 //     channels n = 8*(v/4) + 4*(lane/32) + v%4 of each block: a quantization
@@ -32,10 +33,13 @@
 //     requests; each row's eight 16-byte chunks are rotated by (row / 2) % 8
 //     so that the fragment reads (32 rows x one chunk) are free of bank
 //     conflicts;
-//   - one persistent workgroup per CU walks its tiles; each XCD (its own L2)
-//     runs a contiguous run of tiles, ordered 4 token tiles x all channel
-//     tiles, so that concurrently running workgroups share their A and W
-//     stage tiles in L2, and a tile's stores drain during the next tile.
+//   - one persistent workgroup per CU walks its tiles; the workgroups of an
+//     XCD (its own L2) run 4 token tiles x all channel tiles at a time, so
+//     that they share their A and W stage tiles in L2. For long rows (large
+//     K) all XCDs work on the same rank and channel tiles at once, so that W
+//     is fetched from HBM once and read by the others from the Infinity
+//     Cache; for short rows each XCD takes its own contiguous run of tiles.
+//     A tile's stores drain during the next tile.
 #include <type_traits>
 
 #include "fc_device.h"
@@ -53,18 +57,21 @@ constexpr int kTileT = 256;                 // tokens per workgroup
 constexpr int kTileK = 32;                  // k per stage (2 MFMA steps of 16)
 constexpr int kPairK = 2 * kTileK;          // k per staged pair of stages (128-byte rows)
 constexpr int kPairs = 2;                   // LDS buffers, one pair each
-constexpr int kWaveSpan = 128;              // channels (and tokens) per wave
-constexpr int kBlk = kWaveSpan / 32;        // 32 x 32 MFMA blocks per wave side
+constexpr int kThreads = 512;              // 8 waves, 2 per SIMD
+constexpr int kSpanN = 128;                 // channels per wave
+constexpr int kSpanT = 64;                  // tokens per wave
+constexpr int kBlkN = kSpanN / 32;          // 32 x 32 MFMA blocks per wave, channel side
+constexpr int kBlkT = kSpanT / 32;          // and token side
 constexpr int kWPair = kTileN * kPairK;               // elements of one pair's W tile
 constexpr int kPair = (kTileN + kTileT) * kPairK;    // 16-bit elements per pair buffer (W, then A)
 constexpr int kGroupT = 4;                  // token tiles per scheduling group
 constexpr int kXcds = 8;
+constexpr int kRankMajorMinK = 3072;        // rank-major tile order from this K on
 constexpr int kLdsBytes = 160 * 1024;       // LDS per workgroup on gfx950
 // buffer resource word 3 for raw (untyped, unswizzled) 32-bit-addressed
 // buffers on gfx9-family GPUs
 constexpr int kRawBufferFlags = 0x00020000;
 
-static_assert(kBlockThreads == 256, "four waves per workgroup");
 
 template <int DT>
 __device__ __forceinline__ f32x16 mfma(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
@@ -159,12 +166,12 @@ __device__ __forceinline__ void pair_minmax(float &mn, float &mx) {
 }
 
 template <int DT, int BITS, int G>
-__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void linear_quantize_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int T, int K, int H,
-    int tiles_t, int tiles_n, int total, int grid, uint8_t *__restrict__ codes,
+    int tiles_t, int tiles_n, int total, int grid, int rank_major, uint8_t *__restrict__ codes,
     uint16_t *__restrict__ s, uint16_t *__restrict__ z, uint16_t *__restrict__ y) {
-    static_assert(G >= 8 && G <= kWaveSpan && (G & (G - 1)) == 0, "group of 8..128 channels");
+    static_assert(G >= 8 && G <= kSpanN && (G & (G - 1)) == 0, "group of 8..128 channels");
     // Epilogue staging: a tile's codes (rows padded by 16 bytes to spread the
     // LDS banks), then its scales and zeros. When it fits between the first
     // pair buffer and the end of LDS (all but 8-bit codes in groups of 8), the
@@ -185,15 +192,17 @@ void linear_quantize_kernel(
     const uint32_t tid = __builtin_amdgcn_workitem_id_x();
     const int lane = (int)(tid & 63u);
     const int wave = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
-    const int wn = wave & 1, wt = wave >> 1;
+    const int wn = wave & 1, wt = wave >> 1;   // wt in 0..3
     const uint32_t rowb = (uint32_t)K * 2u;          // bytes per operand row
     const int KT = K / kTileK;                       // stages
     const int KP = (KT + 1) / 2;                     // staged pairs (the last may be half used)
 
-    // Persistent workgroups (`grid` of them, one per CU). Tile order: each
-    // XCD (its own L2) runs a contiguous run of tiles -- workgroup b runs on
-    // XCD b % 8 and takes every (grid/8)-th tile of its XCD's run -- and
-    // within a run kGroupT token tiles x all channel tiles of one rank. A
+    // Persistent workgroups (`grid` of them, one per CU; workgroup b runs on
+    // XCD b % 8). Tile order, within what an XCD runs: kGroupT token tiles x
+    // all channel tiles of one rank, the XCD's workgroups taking consecutive
+    // tiles. What an XCD runs: its own contiguous run of all tiles, or, rank
+    // major (`rank_major`, needs tiles_t % 8 == 0), tiles_t / 8 token tiles
+    // of every rank, all XCDs on the same rank and channel tiles at once. A
     // workgroup's stores of one tile drain while it computes the next.
     const int bid = (int)__builtin_amdgcn_workgroup_id_x();
     const bool by_xcd = total % kXcds == 0 && grid % kXcds == 0;
@@ -206,24 +215,38 @@ void linear_quantize_kernel(
     // The A resource covers only the tile's real token rows: rows past T read
     // as zeros (their outputs are never stored).
     auto tile_at = [&](int it, Tile &tl) -> bool {
-        int logical;
+        // r: the rank; i: the index within a run of `span` token tiles x all
+        // channel tiles starting at token tile `tbase`
+        int r, i, span, tbase;
         if (by_xcd) {
             const int slot = it * (grid / kXcds) + bid / kXcds;
             if (slot >= total / kXcds) return false;
-            logical = (bid % kXcds) * (total / kXcds) + slot;
+            if (rank_major) {
+                span = tiles_t / kXcds;
+                r = slot / (span * tiles_n);
+                i = slot - r * span * tiles_n;
+                tbase = (bid % kXcds) * span;
+            } else {
+                const int logical = (bid % kXcds) * (total / kXcds) + slot;
+                span = tiles_t;
+                r = logical / (tiles_t * tiles_n);
+                i = logical - r * tiles_t * tiles_n;
+                tbase = 0;
+            }
         } else {
-            logical = it * grid + bid;
+            const int logical = it * grid + bid;
             if (logical >= total) return false;
+            span = tiles_t;
+            r = logical / (tiles_t * tiles_n);
+            i = logical - r * tiles_t * tiles_n;
+            tbase = 0;
         }
-        const int per_rank = tiles_t * tiles_n;
-        const int r = logical / per_rank;
-        const int i = logical - r * per_rank;
         const int grp = i / (kGroupT * tiles_n);
         const int first_t = grp * kGroupT;
-        const int gsize = min(tiles_t - first_t, kGroupT);
+        const int gsize = min(span - first_t, kGroupT);
         const int in_grp = i - grp * kGroupT * tiles_n;
         tl.r = r;
-        tl.t0 = (first_t + in_grp % gsize) * kTileT;
+        tl.t0 = (tbase + first_t + in_grp % gsize) * kTileT;
         tl.n0 = (in_grp / gsize) * kTileN;
         const uint16_t *Wb = W + ((size_t)r * H + tl.n0) * (size_t)K;
         const uint16_t *Ab = A + ((size_t)r * T + tl.t0) * (size_t)K;
@@ -237,17 +260,17 @@ void linear_quantize_kernel(
     // 16 bytes land at the instruction's LDS base + 16 i). One instruction
     // fills 8 staged rows of 128 bytes; lane i serves row i / 8 at chunk
     // position i % 8, so it fetches the operand's chunk (i % 8) ^ ((row / 2) %
-    // 8) -- the rotation lds_at reads back. Wave w fills rows w*64 .. w*64+63
-    // of both tiles (8 instructions each, 16 per pair). Addresses are the
-    // tile's buffer resources (SGPRs), a 32-bit lane offset (one for even and
-    // one for odd instructions: the rotation of row w*64 + 8j + i/8 is
-    // (4 (j % 2) + i/16) % 8) and, as the scalar offset, the pair's k offset
-    // plus the instruction's 8 j rows. The last pair of an odd stage count
+    // 8) -- the rotation the fragment reads undo. Wave w fills rows
+    // w*32 .. w*32+31 of both tiles (4 instructions each, 8 per pair).
+    // Addresses are the tile's buffer resources (SGPRs), a 32-bit lane offset
+    // (one for even and one for odd instructions: the rotation of row
+    // w*32 + 8j + i/8 is (4 (j % 2) + i/16) % 8) and, as the scalar offset,
+    // the pair's k offset plus the instruction's 8 j rows. The last pair of an odd stage count
     // also fetches k values past the row's end: those bytes belong to the
     // next row, or lie past the resource and read as zeros, and are never
     // used.
-    constexpr int kLoadsPerPair = 16;            // per wave
-    const uint32_t wrow0 = (uint32_t)wave * 64u;
+    constexpr int kLoadsPerPair = 8;             // per wave
+    const uint32_t wrow0 = (uint32_t)wave * 32u;
     // Per-lane offsets of the staging loads and of the fragment reads (below).
     // They are recomputed from the lane id for every tile and before every
     // batch of staging loads (`fresh` keeps the compiler from hoisting them),
@@ -270,11 +293,11 @@ void linear_quantize_kernel(
         const uint32_t rotx = fhalf ^ ((frow >> 1) & 7u);
         o.cx0 = rotx << 4;
         o.cx1 = (rotx ^ 2u) << 4;
-        o.fbw = (uint32_t)(wn * kWaveSpan + frow) * (kPairK * 2);
-        o.fba = kWPair * 2 + (uint32_t)(wt * kWaveSpan + frow) * (kPairK * 2);
+        o.fbw = (uint32_t)(wn * kSpanN + frow) * (kPairK * 2);
+        o.fba = kWPair * 2 + (uint32_t)(wt * kSpanT + frow) * (kPairK * 2);
         return o;
     };
-    // part nb (0..3) of pair p: instructions j = 2 nb, 2 nb + 1 of both operands
+    // part nb (0..3) of pair p: instruction j = nb of both operands
     auto pair_in_part = [&](const LaneOffs &lo, const Tile &tl, int p, int nb) {
         uint16_t *sw = lds + (p & 1) * kPair;
         uint16_t *sa = sw + kWPair;
@@ -282,14 +305,13 @@ void linear_quantize_kernel(
             const_cast<uint16_t *>(tl.wb), (short)0, (int)(kTileN * rowb), kRawBufferFlags);
         const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t *>(tl.ab), (short)0, (int)tl.abytes, kRawBufferFlags);
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int j = 2 * nb + jj;
+        {
+            const int j = nb;
             const uint32_t l0 = (wrow0 + 8u * j) * kPairK;                // wave-uniform
             const int so = p * (kPairK * 2) + 8 * j * (int)rowb;
             // (a named value: a conditional expression written as the
             // builtin's argument makes the host pass drop the launch stub)
-            const uint32_t vo = jj ? lo.voff_odd : lo.voff_even;
+            const uint32_t vo = (nb & 1) ? lo.voff_odd : lo.voff_even;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 wres, (__attribute__((address_space(3))) void *)(sw + l0), 16, vo, so, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -311,13 +333,23 @@ void linear_quantize_kernel(
     // the pair buffer's and the block's offsets.
     const uint8_t *lbytes = reinterpret_cast<const uint8_t *>(lds);
     // fragments b (W rows and A rows of block b) of step ks of stage kt
-    auto frag_part = [&](const LaneOffs &lo, int kt, int ks, int b, u32x4 (&fw)[kBlk],
-                         u32x4 (&fa)[kBlk]) {
+    auto frag_w = [&](const LaneOffs &lo, int kt, int ks, int b, u32x4 (&fw)[kBlkN]) {
         const uint32_t off = ((ks ? lo.cx1 : lo.cx0) ^ ((uint32_t)(kt & 1) << 6)) +
                              (uint32_t)b * (32 * kPairK * 2);
         const uint32_t pb = (uint32_t)((kt >> 1) & 1);
         fw[b] = *reinterpret_cast<const u32x4 *>(lbytes + lo.fbw + off + pb * (kPair * 2));
+    };
+    auto frag_a = [&](const LaneOffs &lo, int kt, int ks, int b, u32x4 (&fa)[kBlkT]) {
+        const uint32_t off = ((ks ? lo.cx1 : lo.cx0) ^ ((uint32_t)(kt & 1) << 6)) +
+                             (uint32_t)b * (32 * kPairK * 2);
+        const uint32_t pb = (uint32_t)((kt >> 1) & 1);
         fa[b] = *reinterpret_cast<const u32x4 *>(lbytes + lo.fba + off + pb * (kPair * 2));
+    };
+    // the fragments of chunk nb of a step: W block nb, and A block nb while there is one
+    auto frag_part = [&](const LaneOffs &lo, int kt, int ks, int nb, u32x4 (&fw)[kBlkN],
+                         u32x4 (&fa)[kBlkT]) {
+        frag_w(lo, kt, ks, nb, fw);
+        if (nb < kBlkT) frag_a(lo, kt, ks, nb, fa);
     };
 
     Tile cur;
@@ -325,13 +357,13 @@ void linear_quantize_kernel(
     pair_in(cur, 0);
     if (KP > 1) pair_in(cur, 1);
     for (int it = 0;; ++it) {
-        f32x16 acc[kBlk][kBlk];
+        f32x16 acc[kBlkN][kBlkT];
 #pragma unroll
-        for (int a = 0; a < kBlk; ++a)
+        for (int a = 0; a < kBlkN; ++a)
 #pragma unroll
-            for (int b = 0; b < kBlk; ++b) acc[a][b] = f32x16{};
+            for (int b = 0; b < kBlkT; ++b) acc[a][b] = f32x16{};
 
-        // One stage = 2 steps of k = 16, 16 MFMAs each; a pair = 2 stages in
+        // One stage = 2 steps of k = 16, 8 MFMAs each; a pair = 2 stages in
         // one LDS buffer. Pair p + 1 is in flight while pair p is computed:
         // in the middle of stage 2p + 1 this wave waits for its loads of pair
         // p + 1 and the workgroup barrier publishes them (every wave has then
@@ -343,16 +375,16 @@ void linear_quantize_kernel(
         // in flight too.) The wait, the barrier and the issue sit behind
         // uniform branches; the matrix-core work is never under a condition,
         // which would make the compiler spill the accumulators.
-        u32x4 fw[2][kBlk], fa[2][kBlk];
-        // A step in four chunks: chunk nb = the 4 MFMAs of W block nb, then
+        u32x4 fw[2][kBlkN], fa[2][kBlkT];
+        // A step in four chunks: chunk nb = the 2 MFMAs of W block nb, then
         // `side(nb)` (the LDS reads and staging loads that overlap them);
         // nothing moves across chunks, so the loads are spread between the
         // MFMAs.
         auto step = [&](int ks, auto &&side) {
 #pragma unroll
-            for (int nb = 0; nb < kBlk; ++nb) {
+            for (int nb = 0; nb < kBlkN; ++nb) {
 #pragma unroll
-                for (int tb = 0; tb < kBlk; ++tb)
+                for (int tb = 0; tb < kBlkT; ++tb)
                     acc[nb][tb] = mfma<DT>(fw[ks & 1][nb], fa[ks & 1][tb], acc[nb][tb]);
                 side(nb);
                 __builtin_amdgcn_sched_barrier(0);
@@ -365,7 +397,7 @@ void linear_quantize_kernel(
         else wait_loads<0>();
         barrier_keep_loads();
 #pragma unroll
-        for (int b = 0; b < kBlk; ++b) frag_part(lo, 0, 0, b, fw[0], fa[0]);
+        for (int b = 0; b < kBlkN; ++b) frag_part(lo, 0, 0, b, fw[0], fa[0]);
         for (int kt = 0; kt + 1 < KT; ++kt) {
             step(0, [&](int nb) { frag_part(lo, kt, 1, nb, fw[1], fa[1]); });
             const bool odd = (kt & 1) != 0;
@@ -405,15 +437,15 @@ void linear_quantize_kernel(
         const uint32_t lane_y = frow * (uint32_t)H * 2u;
         const int r = cur.r, n0 = cur.n0, t0 = cur.t0;
     #pragma unroll
-        for (int tb = 0; tb < kBlk; ++tb) {
-            const uint32_t tl = (uint32_t)(wt * kWaveSpan + tb * 32) + frow;   // token in the tile
-            const int trow0 = t0 + wt * kWaveSpan + tb * 32;
+        for (int tb = 0; tb < kBlkT; ++tb) {
+            const uint32_t tl = (uint32_t)(wt * kSpanT + tb * 32) + frow;   // token in the tile
+            const int trow0 = t0 + wt * kSpanT + tb * 32;
             const bool live = trow0 + (int)frow < T;
             uint16_t *yb = y ? y + ((size_t)r * T + (size_t)trow0) * (size_t)H +
-                                   (size_t)(n0 + wn * kWaveSpan)
+                                   (size_t)(n0 + wn * kSpanN)
                              : nullptr;
     #pragma unroll
-            for (int gi = 0; gi < kWaveSpan / G; ++gi) {
+            for (int gi = 0; gi < kSpanN / G; ++gi) {
                 // the group's values rounded to the dtype: packed pairs (yw) and
                 // widened back to binary32 (yv) -- what the layer would store
                 float yv[RG][4];
@@ -443,7 +475,7 @@ void linear_quantize_kernel(
                     const int j = gi * RG + jj;
                     const uint32_t ch = (uint32_t)((j / 4) * 32 + (j % 4) * 8) + h4;   // in the wave span
                     const uint32_t q = encode4<BITS>(yv[jj], p);
-                    const uint32_t at = tl * kCodePitch + (wn * kWaveSpan + ch) * BITS / 8;
+                    const uint32_t at = tl * kCodePitch + (wn * kSpanN + ch) * BITS / 8;
                     if constexpr (BITS == 8)
                         *reinterpret_cast<uint32_t *>(lc + at) = q;
                     else
@@ -451,7 +483,7 @@ void linear_quantize_kernel(
                     if (yb && live) stv<u32x2, false>(yb, lane_y + ch * 2u, u32x2{yw[jj][0], yw[jj][1]});
                 }
                 if (fhalf == 0) {
-                    const uint32_t m = tl * kMetaRow + (uint32_t)(wn * (kWaveSpan / G) + gi) * 2u;
+                    const uint32_t m = tl * kMetaRow + (uint32_t)(wn * (kSpanN / G) + gi) * 2u;
                     *reinterpret_cast<uint16_t *>(lsz + m) = p.s16;
                     *reinterpret_cast<uint16_t *>(lsz + kTileT * kMetaRow + m) = p.z16;
                 }
@@ -475,8 +507,8 @@ void linear_quantize_kernel(
         const uint32_t cpitch = (uint32_t)H * BITS / 8;
         constexpr int kCodeChunks = kCodeRow / 16;
     #pragma unroll
-        for (int i = 0; i < kTileT * kCodeChunks / kBlockThreads; ++i) {
-            const uint32_t id = (uint32_t)i * kBlockThreads + wtid;
+        for (int i = 0; i < kTileT * kCodeChunks / kThreads; ++i) {
+            const uint32_t id = (uint32_t)i * kThreads + wtid;
             const uint32_t row = id / kCodeChunks, c = id % kCodeChunks;
             if ((int)row < rows)
                 stg<u32x4>(cg, row * cpitch + c * 16u,
@@ -487,8 +519,8 @@ void linear_quantize_kernel(
         const uint32_t mpitch = (uint32_t)Hg * 2u;
         constexpr int kMetaWords = kMetaRow / 4;         // 4-byte pieces of a row
     #pragma unroll
-        for (int i = 0; i < (kTileT * kMetaWords + kBlockThreads - 1) / kBlockThreads; ++i) {
-            const uint32_t id = (uint32_t)i * kBlockThreads + wtid;
+        for (int i = 0; i < (kTileT * kMetaWords + kThreads - 1) / kThreads; ++i) {
+            const uint32_t id = (uint32_t)i * kThreads + wtid;
             const uint32_t row = id / kMetaWords, c = id % kMetaWords;
             if ((int)row < rows) {
                 const uint32_t at = row * kMetaRow + c * 4u;
@@ -522,9 +554,14 @@ int compute_units() {
     return cached[dev];
 }
 
+// order: 1 rank-major tile order, 0 not, -1 rank-major exactly when K >=
+// kRankMajorMinK (where it was measured faster: at K = 7168 the shared W
+// reads come from the Infinity Cache; at K = 2048 the XCD runs are faster).
+// Rank-major needs the XCD split of the tiles and tiles_t % 8 == 0.
 template <int DT, int BITS, int G>
 hipError_t launch_one(const uint16_t *a, const uint16_t *w, int R, int T, int K, int H,
-                      uint8_t *codes, uint16_t *s, uint16_t *z, uint16_t *y, hipStream_t stream) {
+                      uint8_t *codes, uint16_t *s, uint16_t *z, uint16_t *y, hipStream_t stream,
+                      int order = -1) {
     const int tiles_t = (T + kTileT - 1) / kTileT;
     const int tiles_n = H / kTileN;
     const long long total = (long long)R * tiles_t * tiles_n;
@@ -532,9 +569,11 @@ hipError_t launch_one(const uint16_t *a, const uint16_t *w, int R, int T, int K,
     const int cus = compute_units();
     if (cus <= 0) return hipErrorInvalidDevice;
     const int grid = (int)(total < cus ? total : cus);
+    const bool can_rm = total % kXcds == 0 && grid % kXcds == 0 && tiles_t % kXcds == 0;
+    const int rank_major = can_rm && (order < 0 ? K >= kRankMajorMinK : order != 0);
     hipLaunchKernelGGL((linear_quantize_kernel<DT, BITS, G>), dim3((unsigned)grid),
-                       dim3(kBlockThreads), 0, stream, a, w, T, K, H, tiles_t, tiles_n, (int)total,
-                       grid, codes, s, z, y);
+                       dim3(kThreads), 0, stream, a, w, T, K, H, tiles_t, tiles_n, (int)total,
+                       grid, rank_major, codes, s, z, y);
     return hipGetLastError();
 }
 

@@ -60,9 +60,9 @@ def _bits(v: np.ndarray, dtype: str) -> np.ndarray:
 
 def _dyadic(rng, R, T, K, H, dtype):
     """a = ka/8, w = kw/64 with |ka|, |kw| <= 8 and a few output channels x16:
-    |sum| <= K * 8 * 8 * 16 units of 2^-9 < 2^24 for K <= 2048 -- exact."""
-    ka = rng.integers(-8, 9, size=(R, T, K)).astype(np.float32) / 8
-    kw = rng.integers(-8, 9, size=(R, H, K)).astype(np.float32) / 64
+    |sum| <= K * 8 * 8 * 16 units of 2^-9 < 2^24 for K < 16384 -- exact."""
+    ka = rng.integers(-8, 9, size=(R, T, K), dtype=np.int8).astype(np.float32) / 8
+    kw = rng.integers(-8, 9, size=(R, H, K), dtype=np.int8).astype(np.float32) / 64
     hot = rng.choice(H, size=max(1, H // 100), replace=False)
     kw[:, hot] *= 16
     return _bits(ka, dtype), _bits(kw, dtype)
@@ -87,6 +87,7 @@ EXACT = [  # (R, T, K, H, group, bits, dtype)
     (3, 256, 64, 768, 16, 4, oracle.F16),       # R = 3
     (4, 512, 2048, 8192, 128, 4, oracle.BF16),  # LLaMA-3-70B o_proj per rank, 512 tokens
     (2, 64, 1024, 4096, 128, 8, oracle.F16),    # decode-sized token count
+    (2, 2000, 3072, 512, 64, 8, oracle.F16),    # rank-major tile order (K >= 3072, 8 token tiles), ragged
 ]
 
 
@@ -199,6 +200,22 @@ def test_full_size_sampled_rows():
     a, w = _dyadic(rng, R, T, K, H, dtype)
     got = _run(a, w, dtype, bits, group, want_y=False)
     rows = np.array([0, 1, 255, 256, 4097, 6000, T - 2, T - 1])
+    ref = oracle.linear_quantize(np.ascontiguousarray(a[:, rows]), w, dtype, bits, group)
+    for k in ("codes1", "s1", "z1"):
+        assert np.array_equal(got[k][:, rows], ref[k]), k
+
+
+def test_full_size_d_proj_sampled_rows():
+    """LLaMA-3-70B MLP down projection at full size, one GPU's share of TP = 4
+    (R=4, T=8192, K=28672/4=7168, H=8192, bf16, INT4, g=128): the long-row
+    launch, which walks its tiles rank by rank. Dyadic inputs (exact for
+    K < 16384); sampled rows recomputed by the oracle."""
+    R, T, K, H, group, bits, dtype = 4, 8192, 7168, 8192, 128, 4, oracle.BF16
+    _say("linear_quantize full size 70B d_proj")
+    rng = np.random.default_rng(4343)
+    a, w = _dyadic(rng, R, T, K, H, dtype)
+    got = _run(a, w, dtype, bits, group, want_y=False)
+    rows = np.array([0, 255, 256, 2047, 2048, 5000, T - 1])
     ref = oracle.linear_quantize(np.ascontiguousarray(a[:, rows]), w, dtype, bits, group)
     for k in ("codes1", "s1", "z1"):
         assert np.array_equal(got[k][:, rows], ref[k]), k
