@@ -66,6 +66,7 @@ def link_bytes(R: int, T: int, H: int, bits: int, group: int, group2: int, e: in
 
 K1_SAMPLE_EVERY = 10
 GRAPH_CALLS = 20       # calls captured per HIP graph in the launch-bound measurements
+LINEAR_ROUNDS = 3      # interleaved timing rounds of the linear-layer variants
 
 
 def k1_sample_every(steps: int) -> int:
@@ -443,16 +444,19 @@ def main() -> int:
 
             flops = 2.0 * R * T * H * Kl
             n_it = max(3, min(20, int(2e13 / flops)))
-            lin_ms = timed(fused_lin, n_it)
-            gemm_ms = timed(gemm_only, n_it)
-            unf_ms = timed(unfused_lin, n_it)
+            # three rounds, the variants interleaved, median per variant: the
+            # first launches after a change of shape or kernel run slower
+            rounds = [[timed(fn, n_it) for fn in (fused_lin, gemm_only, unfused_lin)]
+                      for _ in range(LINEAR_ROUNDS)]
+            lin_ms, gemm_ms, unf_ms = (sorted(col)[len(col) // 2] for col in zip(*rounds))
             tf = flops / (lin_ms * 1e-3) / 1e12
             linear[name] = {
                 "shape": {"R": R, "T": T, "K": Kl, "H": H},
                 "fused_ms": round(lin_ms, 4),
                 "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                             "timing": f"HIP events around {n_it} back-to-back launches"},
+                             "timing": f"HIP events around {n_it} back-to-back launches, median of "
+                                       f"{LINEAR_ROUNDS} rounds interleaved with the unfused variants"},
                 "torch_gemm_ms": round(gemm_ms, 4),
                 "torch_gemm_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
                 "unfused_ms": round(unf_ms, 4),
