@@ -269,6 +269,7 @@ def main() -> int:
     print(f"[bench] generating {w.name}: R={R} T={T} H={H} {w.dtype} int{bits} g{group}",
           file=sys.stderr, flush=True)
     x_host = synth.operands(w, args.seed)
+    x_checksum = synth.checksum(x_host)
 
     # Two buffer sets used in turn, so a step never finds the previous step's
     # inputs or payloads in the caches.
@@ -509,10 +510,17 @@ def main() -> int:
         "kernel_ms_median": {"k1_quantize": round(float(k_med[0]), 5),
                              "k2_dequant_sum_requant": round(float(k_med[1]), 5),
                              "k3_dequantize": round(float(k_med[2]), 5)},
+        "kernel_ms_p10_p90": {name: [round(float(np.percentile(k_ms[:, j], 10)), 5),
+                                     round(float(np.percentile(k_ms[:, j], 90)), 5)]
+                              for j, name in enumerate(("k1_quantize", "k2_dequant_sum_requant",
+                                                        "k3_dequantize"))},
         "kernel_gbps": {"k1_quantize": round(mb["k1"] / (k_avg[0] * 1e-3) / 1e9, 1),
                         "k2_dequant_sum_requant": round(mb["k2"] / (k_avg[1] * 1e-3) / 1e9, 1),
                         "k3_dequantize": round(mb["k3"] / (k_avg[2] * 1e-3) / 1e9, 1)},
         "pipeline_ms_median_events": round(float(np.median(pipe_ms)), 5),
+        "pipeline_ms_p10_p90_events": [round(float(np.percentile(pipe_ms, 10)), 5),
+                                       round(float(np.percentile(pipe_ms, 90)), 5)],
+        "input_checksum": {"seed": args.seed, "blake2b_64": x_checksum},
         "copy_ceiling_gbps": round(copy_gbps, 1),
         "uncompressed_sum": {"ms": round(sum_ms, 5), "bytes": sum_bytes,
                              "gbps": round(sum_bytes / (sum_ms * 1e-3) / 1e9, 1),
