@@ -57,7 +57,7 @@ constexpr int kTileT = 256;                 // tokens per workgroup
 constexpr int kTileK = 32;                  // k per stage (2 MFMA steps of 16)
 constexpr int kPairK = 2 * kTileK;          // k per staged pair of stages (128-byte rows)
 constexpr int kPairs = 2;                   // LDS buffers, one pair each
-constexpr int kThreads = 512;              // 8 waves, 2 per SIMD
+constexpr int kThreads = 512;               // 8 waves, 2 per SIMD
 constexpr int kSpanN = 128;                 // channels per wave
 constexpr int kSpanT = 64;                  // tokens per wave
 constexpr int kBlkN = kSpanN / 32;          // 32 x 32 MFMA blocks per wave, channel side
