@@ -34,12 +34,14 @@
 //     so that the fragment reads (32 rows x one chunk) are free of bank
 //     conflicts;
 //   - one persistent workgroup per CU walks its tiles; the workgroups of an
-//     XCD (its own L2) run 4 token tiles x all channel tiles at a time, so
+//     XCD (its own L2) run 4 token tiles x 8 channel tiles at a time, so
 //     that they share their A and W stage tiles in L2. For long rows (large
-//     K) all XCDs work on the same rank and channel tiles at once, so that W
-//     is fetched from HBM once and read by the others from the Infinity
-//     Cache; for short rows each XCD takes its own contiguous run of tiles.
-//     A tile's stores drain during the next tile.
+//     K) the 8 XCDs form a 4 x 2 grid over each rank's tiles (token quarters
+//     x channel halves), all on the same rank at once: an A tile is read by
+//     2 XCDs and a W tile by 4 at about the same time, one of them from HBM
+//     and the others from the Infinity Cache. For short rows each XCD takes
+//     its own contiguous run of tiles. A tile's stores drain during the next
+//     tile.
 #include <type_traits>
 
 #include "fc_device.h"
@@ -66,7 +68,8 @@ constexpr int kWPair = kTileN * kPairK;               // elements of one pair's 
 constexpr int kPair = (kTileN + kTileT) * kPairK;    // 16-bit elements per pair buffer (W, then A)
 constexpr int kGroupT = 4;                  // token tiles per scheduling group
 constexpr int kXcds = 8;
-constexpr int kRankMajorMinK = 3072;        // rank-major tile order from this K on
+constexpr int kGridT = 4;                   // XCD grid: token groups (x channel groups kXcds / kGridT)
+constexpr int kGridMinK = 3072;             // XCD-grid tile order from this K on
 constexpr int kLdsBytes = 160 * 1024;       // LDS per workgroup on gfx950
 // buffer resource word 3 for raw (untyped, unswizzled) 32-bit-addressed
 // buffers on gfx9-family GPUs
@@ -169,7 +172,7 @@ template <int DT, int BITS, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void linear_quantize_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int T, int K, int H,
-    int tiles_t, int tiles_n, int total, int grid, int rank_major, uint8_t *__restrict__ codes,
+    int tiles_t, int tiles_n, int total, int grid, int xcd_grid, uint8_t *__restrict__ codes,
     uint16_t *__restrict__ s, uint16_t *__restrict__ z, uint16_t *__restrict__ y) {
     static_assert(G >= 8 && G <= kSpanN && (G & (G - 1)) == 0, "group of 8..128 channels");
     // Epilogue staging: a tile's codes (rows padded by 16 bytes to spread the
@@ -198,12 +201,13 @@ void linear_quantize_kernel(
     const int KP = (KT + 1) / 2;                     // staged pairs (the last may be half used)
 
     // Persistent workgroups (`grid` of them, one per CU; workgroup b runs on
-    // XCD b % 8). Tile order, within what an XCD runs: kGroupT token tiles x
-    // all channel tiles of one rank, the XCD's workgroups taking consecutive
-    // tiles. What an XCD runs: its own contiguous run of all tiles, or, rank
-    // major (`rank_major`, needs tiles_t % 8 == 0), tiles_t / 8 token tiles
-    // of every rank, all XCDs on the same rank and channel tiles at once. A
-    // workgroup's stores of one tile drain while it computes the next.
+    // XCD b % 8). What an XCD runs: its own contiguous run of all tiles, or,
+    // on the XCD grid (`xcd_grid`, needs tiles_t % 4 == 0 and tiles_n % 2 ==
+    // 0), XCD x takes token quarter x % 4 and channel half x / 4 of every
+    // rank, rank by rank. Within that, the XCD's workgroups take consecutive
+    // tiles of kGroupT token tiles x the channel tiles of its share, one rank
+    // at a time. A workgroup's stores of one tile drain while it computes the
+    // next.
     const int bid = (int)__builtin_amdgcn_workgroup_id_x();
     const bool by_xcd = total % kXcds == 0 && grid % kXcds == 0;
     struct Tile {
@@ -215,17 +219,20 @@ void linear_quantize_kernel(
     // The A resource covers only the tile's real token rows: rows past T read
     // as zeros (their outputs are never stored).
     auto tile_at = [&](int it, Tile &tl) -> bool {
-        // r: the rank; i: the index within a run of `span` token tiles x all
-        // channel tiles starting at token tile `tbase`
-        int r, i, span, tbase;
+        // r: the rank; i: the index within a share of `span` token tiles from
+        // `tbase` x `span_n` channel tiles from `nbase`
+        int r, i, span, tbase, span_n = tiles_n, nbase = 0;
         if (by_xcd) {
             const int slot = it * (grid / kXcds) + bid / kXcds;
             if (slot >= total / kXcds) return false;
-            if (rank_major) {
-                span = tiles_t / kXcds;
-                r = slot / (span * tiles_n);
-                i = slot - r * span * tiles_n;
-                tbase = (bid % kXcds) * span;
+            if (xcd_grid) {
+                const int x = bid % kXcds;
+                span = tiles_t / kGridT;
+                span_n = tiles_n / (kXcds / kGridT);
+                r = slot / (span * span_n);
+                i = slot - r * span * span_n;
+                tbase = (x % kGridT) * span;
+                nbase = (x / kGridT) * span_n;
             } else {
                 const int logical = (bid % kXcds) * (total / kXcds) + slot;
                 span = tiles_t;
@@ -241,13 +248,13 @@ void linear_quantize_kernel(
             i = logical - r * tiles_t * tiles_n;
             tbase = 0;
         }
-        const int grp = i / (kGroupT * tiles_n);
+        const int grp = i / (kGroupT * span_n);
         const int first_t = grp * kGroupT;
         const int gsize = min(span - first_t, kGroupT);
-        const int in_grp = i - grp * kGroupT * tiles_n;
+        const int in_grp = i - grp * kGroupT * span_n;
         tl.r = r;
         tl.t0 = (tbase + first_t + in_grp % gsize) * kTileT;
-        tl.n0 = (in_grp / gsize) * kTileN;
+        tl.n0 = (nbase + in_grp / gsize) * kTileN;
         const uint16_t *Wb = W + ((size_t)r * H + tl.n0) * (size_t)K;
         const uint16_t *Ab = A + ((size_t)r * T + tl.t0) * (size_t)K;
         tl.abytes = (uint32_t)min(kTileT, T - tl.t0) * rowb;
@@ -554,10 +561,11 @@ int compute_units() {
     return cached[dev];
 }
 
-// order: 1 rank-major tile order, 0 not, -1 rank-major exactly when K >=
-// kRankMajorMinK (where it was measured faster: at K = 7168 the shared W
-// reads come from the Infinity Cache; at K = 2048 the XCD runs are faster).
-// Rank-major needs the XCD split of the tiles and tiles_t % 8 == 0.
+// order: 1 the XCD-grid tile order, 0 the XCD runs, -1 the grid exactly when
+// K >= kGridMinK (measured on the 70B layer shapes, K = 2048 ... 7168: the
+// grid is 2-5% faster from K = 3072 on, where the shared reads come from the
+// Infinity Cache; at K = 2048 the XCD runs are 2% faster). The grid needs the
+// XCD split of the tiles, tiles_t % 4 == 0 and tiles_n % 2 == 0.
 template <int DT, int BITS, int G>
 hipError_t launch_one(const uint16_t *a, const uint16_t *w, int R, int T, int K, int H,
                       uint8_t *codes, uint16_t *s, uint16_t *z, uint16_t *y, hipStream_t stream,
@@ -569,11 +577,12 @@ hipError_t launch_one(const uint16_t *a, const uint16_t *w, int R, int T, int K,
     const int cus = compute_units();
     if (cus <= 0) return hipErrorInvalidDevice;
     const int grid = (int)(total < cus ? total : cus);
-    const bool can_rm = total % kXcds == 0 && grid % kXcds == 0 && tiles_t % kXcds == 0;
-    const int rank_major = can_rm && (order < 0 ? K >= kRankMajorMinK : order != 0);
+    const bool can_grid = total % kXcds == 0 && grid % kXcds == 0 && tiles_t % kGridT == 0 &&
+                          tiles_n % (kXcds / kGridT) == 0;
+    const int xcd_grid = can_grid && (order < 0 ? K >= kGridMinK : order != 0);
     hipLaunchKernelGGL((linear_quantize_kernel<DT, BITS, G>), dim3((unsigned)grid),
                        dim3(kThreads), 0, stream, a, w, T, K, H, tiles_t, tiles_n, (int)total,
-                       grid, rank_major, codes, s, z, y);
+                       grid, xcd_grid, codes, s, z, y);
     return hipGetLastError();
 }
 

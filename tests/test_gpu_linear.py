@@ -87,7 +87,7 @@ EXACT = [  # (R, T, K, H, group, bits, dtype)
     (3, 256, 64, 768, 16, 4, oracle.F16),       # R = 3
     (4, 512, 2048, 8192, 128, 4, oracle.BF16),  # LLaMA-3-70B o_proj per rank, 512 tokens
     (2, 64, 1024, 4096, 128, 8, oracle.F16),    # decode-sized token count
-    (2, 2000, 3072, 512, 64, 8, oracle.F16),    # rank-major tile order (K >= 3072, 8 token tiles), ragged
+    (2, 2000, 3072, 512, 64, 8, oracle.F16),    # XCD-grid tile order (K >= 3072), ragged tokens
 ]
 
 
@@ -208,7 +208,7 @@ def test_full_size_sampled_rows():
 def test_full_size_d_proj_sampled_rows():
     """LLaMA-3-70B MLP down projection at full size, one GPU's share of TP = 4
     (R=4, T=8192, K=28672/4=7168, H=8192, bf16, INT4, g=128): the long-row
-    launch, which walks its tiles rank by rank. Dyadic inputs (exact for
+    launch, which takes its tiles on the XCD grid. Dyadic inputs (exact for
     K < 16384); sampled rows recomputed by the oracle."""
     R, T, K, H, group, bits, dtype = 4, 8192, 7168, 8192, 128, 4, oracle.BF16
     _say("linear_quantize full size 70B d_proj")
