@@ -88,6 +88,9 @@ EXACT = [  # (R, T, K, H, group, bits, dtype)
     (4, 512, 2048, 8192, 128, 4, oracle.BF16),  # LLaMA-3-70B o_proj per rank, 512 tokens
     (2, 64, 1024, 4096, 128, 8, oracle.F16),    # decode-sized token count
     (2, 2000, 3072, 512, 64, 8, oracle.F16),    # XCD-grid tile order (K >= 3072), ragged tokens
+    (1, 1000, 3200, 512, 32, 4, oracle.BF16),   # XCD grid with one tile per XCD
+    (2, 2048, 3136, 1024, 16, 4, oracle.F16),   # XCD grid, 2 x 2 tiles per XCD and rank
+    (3, 1024, 3104, 768, 128, 8, oracle.F16),   # K >= 3072 but 3 channel tiles: XCD runs; odd stage count
 ]
 
 
