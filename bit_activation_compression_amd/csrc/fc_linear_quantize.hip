@@ -203,10 +203,10 @@ void linear_quantize_kernel(
     // Persistent workgroups (`grid` of them, one per CU; workgroup b runs on
     // XCD b % 8). What an XCD runs: its own contiguous run of all tiles, or,
     // on the XCD grid (`xcd_grid`, needs tiles_t % 4 == 0 and tiles_n % 2 ==
-    // 0), XCD x takes token quarter x % 4 and channel half x / 4 of every
-    // rank, rank by rank. Within that, the XCD's workgroups take consecutive
-    // tiles of kGroupT token tiles x the channel tiles of its share, one rank
-    // at a time. A workgroup's stores of one tile drain while it computes the
+    // 0), token quarter x % 4 x channel half x / 4 of each rank (XCD x), rank
+    // after rank. Within its share, the XCD's workgroups take consecutive
+    // tiles in groups of kGroupT token tiles x all channel tiles of the
+    // share. A workgroup's stores of one tile drain while it computes the
     // next.
     const int bid = (int)__builtin_amdgcn_workgroup_id_x();
     const bool by_xcd = total % kXcds == 0 && grid % kXcds == 0;
