@@ -42,6 +42,7 @@
 //     and the others from the Infinity Cache. For short rows each XCD takes
 //     its own contiguous run of tiles. A tile's stores drain during the next
 //     tile.
+#include <atomic>
 #include <type_traits>
 
 #include "fc_device.h"
@@ -547,18 +548,20 @@ void linear_quantize_kernel(
 }
 
 // Compute units of the current device (one persistent workgroup each),
-// looked up once per device.
+// looked up once per device. The cache is atomic: calls from several host
+// threads may fill it at once (with the same value).
 int compute_units() {
-    static int cached[64] = {};
+    static std::atomic<int> cached[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-    if (cached[dev] <= 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
             return -1;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 // order: 1 the XCD-grid tile order, 0 the XCD runs, -1 the grid exactly when

@@ -38,7 +38,8 @@
  *   - Non-finite inputs, or inputs whose scale or zero overflow fp16
  *     (|min| > 65504 or (max - min)/Q > 65504), are outside the contract:
  *     the results are unspecified but every access stays in bounds.
- *   - No global state: concurrent calls on different streams are safe.
+ *   - No global state beyond a per-device cache of the compute-unit count
+ *     (atomic): concurrent calls on different streams are safe.
  *
  * Supported shapes (FC_ERR_SHAPE otherwise): R >= 1, T >= 0, H >= 1,
  * bits in {4, 8} (FC_ERR_BITS), group a power of two in [8, 8192] dividing H,
