@@ -91,6 +91,8 @@ EXACT = [  # (R, T, K, H, group, bits, dtype)
     (1, 1000, 3200, 512, 32, 4, oracle.BF16),   # XCD grid with one tile per XCD
     (2, 2048, 3136, 1024, 16, 4, oracle.F16),   # XCD grid, 2 x 2 tiles per XCD and rank
     (3, 1024, 3104, 768, 128, 8, oracle.F16),   # K >= 3072 but 3 channel tiles: XCD runs; odd stage count
+    (2, 300, 352, 512, 8, 4, oracle.F16),       # 4-bit codes in groups of 8 (staging loads in one burst), 11 stages
+    (1, 700, 160, 256, 8, 4, oracle.BF16),      # the same, bf16, 5 stages
 ]
 
 
