@@ -51,12 +51,14 @@ __device__ __forceinline__ void lanes_minmax_any(float (&mn)[N], float (&mx)[N],
     }
 }
 
-// A stage boundary inside the kernel: this wave's stores of a payload are
-// complete and the payload is then read back from memory (release, then
-// acquire, at device scope: the stores reach L2, the vector L1 is
-// invalidated). Each wave reads back only what it wrote itself -- every
-// position depends only on the same position of the operands -- so no other
-// wave's progress is involved.
+// A stage boundary inside the kernel: the payload this wave has just stored
+// is read back from memory (release, then acquire, at workgroup scope). Each
+// wave reads back only what it wrote itself -- every position depends only
+// on the same position of the operands -- so no other wave's progress is
+// involved, and the wave's stores and later loads go in order through its
+// CU's vector memory path: the fences only keep the compiler from moving
+// loads above the stores, and no cache write-back or invalidation is needed
+// (a device-scope fence would write L2 back for nothing).
 __device__ __forceinline__ void handoff() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
