@@ -18,6 +18,10 @@ constexpr int kMaxGroup = 8192;
 constexpr int kLinearTileN = 256;
 constexpr int kLinearTileK = 32;
 constexpr int kLinearMaxGroup = 128;
+// and the largest K and H whose tile offsets fit the kernel's 32-bit buffer
+// and lane offsets (256 rows of 2K bytes; 256 token rows of H codes)
+constexpr int kLinearMaxK = 1 << 22;
+constexpr int kLinearMaxH = 1 << 24;
 
 bool pow2_in_range(int g) { return g >= kMinGroup && g <= kMaxGroup && (g & (g - 1)) == 0; }
 
@@ -230,8 +234,8 @@ fc_status fc_linear_quantize(const void *a, const void *w, fc_dtype dt, int R, i
     int g2 = 0;
     fc_status st = check_shape(R, T, H, bits, group, &g2);
     if (st != FC_OK) return st;
-    if (K < kLinearTileK || K % kLinearTileK != 0 || H % kLinearTileN != 0 ||
-        group > kLinearMaxGroup)
+    if (K < kLinearTileK || K % kLinearTileK != 0 || K > kLinearMaxK || H % kLinearTileN != 0 ||
+        H > kLinearMaxH || group > kLinearMaxGroup)
         return FC_ERR_SHAPE;
     if (dt != FC_F16 && dt != FC_BF16) return FC_ERR_DTYPE;
     const uint64_t n = (uint64_t)R * (uint64_t)T * (uint64_t)H;
