@@ -125,6 +125,23 @@ def _dev_tensor(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _dt(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"{name} must be float16 or bfloat16, not {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def _room(t: torch.Tensor, name: str, nbytes: int, device) -> None:
+    """A caller's buffer: a contiguous tensor on `device` of at least `nbytes`
+    bytes (the library writes or reads that many through a raw pointer)."""
+    _dev_tensor(t, name)
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, {nbytes} needed")
+
+
 def fc_status_string(status: int) -> str:
     return lib().fc_status_string(status).decode()
 
@@ -164,7 +181,10 @@ def fc_quantize_groups(x: torch.Tensor, bits: int, group: int, codes1=None, s1=N
         s1 = torch.empty((R, T, max(H // group, 0)), dtype=torch.uint16, device=dev)
     if z1 is None:
         z1 = torch.empty_like(s1)
-    _check(lib().fc_quantize_groups(_ptr(x), _DTYPES[x.dtype], R, T, H, bits, group, _ptr(codes1),
+    _room(codes1, "codes1", R * T * H * bits // 8, dev)
+    _room(s1, "s1", R * T * (H // group) * 2, dev)
+    _room(z1, "z1", R * T * (H // group) * 2, dev)
+    _check(lib().fc_quantize_groups(_ptr(x), _dt(x, "x"), R, T, H, bits, group, _ptr(codes1),
                                     _ptr(s1), _ptr(z1), _stream(stream, dev)), "fc_quantize_groups")
     return codes1, s1, z1
 
@@ -183,6 +203,12 @@ def fc_dequant_sum_requant(codes1, s1, z1, R: int, T: int, H: int, bits: int, gr
         s2 = torch.empty((T, H // g2 if g2 else 0), dtype=torch.uint16, device=dev)
     if z2 is None:
         z2 = torch.empty_like(s2)
+    _room(codes1, "codes1", R * T * H * bits // 8, dev)
+    _room(s1, "s1", R * T * (H // group) * 2, dev)
+    _room(z1, "z1", R * T * (H // group) * 2, dev)
+    _room(codes2, "codes2", T * H * bits2 // 8, dev)
+    _room(s2, "s2", T * (H // g2 if g2 else 0) * 2, dev)
+    _room(z2, "z2", T * (H // g2 if g2 else 0) * 2, dev)
     if bits2 == bits:
         st = lib().fc_dequant_sum_requant(_ptr(codes1), _ptr(s1), _ptr(z1), R, T, H, bits, group,
                                           _ptr(codes2), _ptr(s2), _ptr(z2), _stream(stream, dev))
@@ -202,8 +228,12 @@ def fc_dequantize(codes2, s2, z2, T: int, H: int, bits: int, group2: int, dtype:
     dev = codes2.device
     if out is None:
         out = torch.empty((T, H), dtype=dtype, device=dev)
+    _room(codes2, "codes2", T * H * bits // 8, dev)
+    _room(s2, "s2", T * (H // group2 if group2 > 0 else 0) * 2, dev)
+    _room(z2, "z2", T * (H // group2 if group2 > 0 else 0) * 2, dev)
+    _room(out, "out", T * H * 2, dev)
     _check(lib().fc_dequantize(_ptr(codes2), _ptr(s2), _ptr(z2), T, H, bits, group2,
-                               _DTYPES[out.dtype], _ptr(out), _stream(stream, dev)), "fc_dequantize")
+                               _dt(out, "out"), _ptr(out), _stream(stream, dev)), "fc_dequantize")
     return out
 
 
@@ -229,9 +259,12 @@ def fc_linear_quantize(a: torch.Tensor, w: torch.Tensor, bits: int, group: int, 
         z1 = torch.empty_like(s1)
     if y is True:
         y = torch.empty((R, T, H), dtype=a.dtype, device=dev)
-    elif y is not None:
-        _dev_tensor(y, "y")
-    _check(lib().fc_linear_quantize(_ptr(a), _ptr(w), _DTYPES[a.dtype], R, T, K, H, bits, group,
+    _room(codes1, "codes1", R * T * H * bits // 8, dev)
+    _room(s1, "s1", R * T * (H // group) * 2, dev)
+    _room(z1, "z1", R * T * (H // group) * 2, dev)
+    if y is not None:
+        _room(y, "y", R * T * H * 2, dev)
+    _check(lib().fc_linear_quantize(_ptr(a), _ptr(w), _dt(a, "a"), R, T, K, H, bits, group,
                                     _ptr(codes1), _ptr(s1), _ptr(z1), _ptr(y),
                                     _stream(stream, dev)), "fc_linear_quantize")
     return codes1, s1, z1, y
@@ -248,8 +281,13 @@ def fc_dequantize_residual(codes2, s2, z2, T: int, H: int, bits: int, group2: in
         out = torch.empty((T, H), dtype=residual.dtype, device=dev)
     if out.dtype != residual.dtype:
         raise ValueError("out and residual must have the same dtype")
+    _room(codes2, "codes2", T * H * bits // 8, dev)
+    _room(s2, "s2", T * (H // group2 if group2 > 0 else 0) * 2, dev)
+    _room(z2, "z2", T * (H // group2 if group2 > 0 else 0) * 2, dev)
+    _room(residual, "residual", T * H * 2, dev)
+    _room(out, "out", T * H * 2, dev)
     _check(lib().fc_dequantize_residual(_ptr(codes2), _ptr(s2), _ptr(z2), T, H, bits, group2,
-                                        _DTYPES[residual.dtype], _ptr(residual), _ptr(out),
+                                        _dt(residual, "residual"), _ptr(residual), _ptr(out),
                                         _stream(stream, dev)), "fc_dequantize_residual")
     return out
 
@@ -268,20 +306,24 @@ def fc_allreduce_emulated(x: torch.Tensor, bits: int, group: int, out=None, work
     if workspace is None:
         workspace = torch.empty(max(fc_workspace_bytes(R, T, H, bits, group, bits2), 1),
                                 dtype=torch.uint8, device=dev)
+    if out.dtype != x.dtype:
+        raise ValueError("out must have x's dtype")
+    _room(out, "out", T * H * 2, dev)
+    _room(workspace, "workspace", 0, dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
     if residual is not None:
         _dev_tensor(residual, "residual")
         if residual.dtype != x.dtype or tuple(residual.shape) != (T, H):
             raise ValueError("residual must be [T, H] of x's dtype")
-        st = lib().fc_allreduce_emulated_residual(_ptr(x), _DTYPES[x.dtype], R, T, H, bits, bits2,
+        st = lib().fc_allreduce_emulated_residual(_ptr(x), _dt(x, "x"), R, T, H, bits, bits2,
                                                   group, _ptr(residual), _ptr(out),
-                                                  _ptr(workspace), workspace.numel(),
-                                                  _stream(stream, dev))
+                                                  _ptr(workspace), ws_bytes, _stream(stream, dev))
     elif bits2 == bits:
-        st = lib().fc_allreduce_emulated(_ptr(x), _DTYPES[x.dtype], R, T, H, bits, group, _ptr(out),
-                                         _ptr(workspace), workspace.numel(), _stream(stream, dev))
+        st = lib().fc_allreduce_emulated(_ptr(x), _dt(x, "x"), R, T, H, bits, group, _ptr(out),
+                                         _ptr(workspace), ws_bytes, _stream(stream, dev))
     else:
-        st = lib().fc_allreduce_emulated_mixed(_ptr(x), _DTYPES[x.dtype], R, T, H, bits, bits2, group,
-                                               _ptr(out), _ptr(workspace), workspace.numel(),
+        st = lib().fc_allreduce_emulated_mixed(_ptr(x), _dt(x, "x"), R, T, H, bits, bits2, group,
+                                               _ptr(out), _ptr(workspace), ws_bytes,
                                                _stream(stream, dev))
     _check(st, "fc_allreduce_emulated")
     return out, workspace
@@ -293,7 +335,10 @@ def fc_sum_uncompressed(x: torch.Tensor, out=None, stream=None):
     R, T, H = x.shape
     if out is None:
         out = torch.empty((T, H), dtype=x.dtype, device=x.device)
-    _check(lib().fc_sum_uncompressed(_ptr(x), _DTYPES[x.dtype], R, T, H, _ptr(out),
+    if out.dtype != x.dtype:
+        raise ValueError("out must have x's dtype")
+    _room(out, "out", T * H * 2, x.device)
+    _check(lib().fc_sum_uncompressed(_ptr(x), _dt(x, "x"), R, T, H, _ptr(out),
                                      _stream(stream, x.device)), "fc_sum_uncompressed")
     return out
 
