@@ -128,7 +128,7 @@ def _draw_linear(rng):
     return R, T, K, H, group, bits, dtype
 
 
-RANDOM = [_draw_linear(np.random.default_rng(77 + i)) for i in range(16)]
+RANDOM = [_draw_linear(np.random.default_rng(77 + i)) for i in range(32)]
 
 
 @pytest.mark.parametrize("R,T,K,H,group,bits,dtype", RANDOM)

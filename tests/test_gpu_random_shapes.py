@@ -74,7 +74,7 @@ def _draw(rng) -> tuple:
         return R, T, H, group, bits, bits2, dtype, bool(rng.random() < 0.3)
 
 
-CASES = [_draw(np.random.default_rng(2024 + i)) for i in range(40)]
+CASES = [_draw(np.random.default_rng(2024 + i)) for i in range(100)]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"R{c[0]}T{c[1]}H{c[2]}g{c[3]}b{c[4]}{c[5]}{c[6]}{'r' if c[7] else ''}"
