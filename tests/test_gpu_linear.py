@@ -185,6 +185,26 @@ def test_normal_inputs(R, T, K, H, group, bits, dtype):
     assert np.array_equal(_np(s2), got["s1"]) and np.array_equal(_np(z2), got["z1"])
 
 
+@pytest.mark.parametrize("bits,dtype", [(4, oracle.BF16), (8, oracle.F16)])
+def test_degenerate_groups(bits, dtype):
+    """Output groups whose values are all equal: zero weight rows give groups
+    of zeros (scale 0), equal weight rows give constant nonzero groups, and
+    a zero token row gives a whole row of zeros."""
+    R, T, K, H, group = 2, 300, 96, 512, 128
+    _say(f"linear_quantize degenerate groups int{bits} {dtype}")
+    rng = np.random.default_rng(31)
+    a, w = _dyadic(rng, R, T, K, H, dtype)
+    w[:, 0:128] = _bits(np.zeros((R, 128, K), dtype=np.float32), dtype)          # y = 0
+    w[:, 128:256] = w[:, 128:129]                                                  # equal channels
+    a[:, 7] = _bits(np.zeros((R, K), dtype=np.float32), dtype)                    # a zero token row
+    ref = oracle.linear_quantize(a, w, dtype, bits, group)
+    got = _run(a, w, dtype, bits, group)
+    assert np.array_equal(got["y"], ref["y"])
+    for k in ("codes1", "s1", "z1"):
+        assert np.array_equal(got[k], ref[k]), k
+    assert np.all(ref["s1"][:, :, 0] == 0) and np.all(ref["s1"][:, :, 1] == 0)   # the cases are hit
+
+
 def test_empty_token_dimension():
     _say("linear_quantize T=0")
     a = torch.empty((4, 0, 2048), dtype=torch.bfloat16, device="cuda")

@@ -229,7 +229,8 @@ def test_edge_groups(dtype, bits):
     w = synth.workload("tiny").with_(name="edge", R=4, T=8, H=512, bits=bits, group=128, dtype=dtype)
     ref = oracle.allreduce(x, dtype, bits, 128, want_f32=False)
     _say(f"edge groups {dtype} bits={bits}")
-    _check(_run_fused(x, w), ref, w, x)
+    _check(_run_fused(x, w), ref, w, x)          # the single launch (R*T*H <= 2^24)
+    _check(_run_steps(x, w), ref, w, x)          # the three stage kernels
 
 
 # ---------------------------------------------------------------------------
