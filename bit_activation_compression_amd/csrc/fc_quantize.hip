@@ -15,7 +15,7 @@
 namespace fc {
 namespace {
 
-// Tiles of 4 slots (8 KiB of input per wave) with non-temporal loads and
+// Tiles of 4 slots (4 KiB of input per wave) with non-temporal loads and
 // code stores measured fastest on MI355X for this read-4 / write-1 stream,
 // counting the effect on the kernel that reads the codes next.
 constexpr int kTileSlots = 4;
