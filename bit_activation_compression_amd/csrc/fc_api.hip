@@ -13,11 +13,11 @@ namespace {
 constexpr size_t kSliceAlign = 256;
 constexpr int kMinGroup = 8;
 constexpr int kMaxGroup = 8192;
-// fc_linear_quantize: channel tile, k stage and the largest group one lane
-// pair of its matrix-core tile holds
+// fc_linear_quantize: channel tile, k stage and the largest group (one
+// channel tile row)
 constexpr int kLinearTileN = 256;
 constexpr int kLinearTileK = 32;
-constexpr int kLinearMaxGroup = 128;
+constexpr int kLinearMaxGroup = 256;
 // and the largest K and H whose tile offsets fit the kernel's 32-bit buffer
 // and lane offsets (256 rows of 2K bytes; 256 token rows of H codes)
 constexpr int kLinearMaxK = 1 << 22;

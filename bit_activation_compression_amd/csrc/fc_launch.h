@@ -34,7 +34,7 @@ hipError_t launch_dequantize_residual(const uint8_t *codes2, const uint16_t *s2,
 
 // Row-parallel linear layer y[r] = a[r] w[r]^T (a [R][T][K], w [R][H][K]) with
 // the stage-1 quantization of y in its epilogue (H % 256 == 0, K % 32 == 0,
-// group in {8, 16, 32, 64, 128}); y itself is written only when y != NULL.
+// group in {8, ..., 256}); y itself is written only when y != NULL.
 hipError_t launch_linear_quantize(const uint16_t *a, const uint16_t *w, int dtype, int R, int T,
                                   int K, int H, int bits, int group, uint8_t *codes, uint16_t *s,
                                   uint16_t *z, uint16_t *y, hipStream_t stream);

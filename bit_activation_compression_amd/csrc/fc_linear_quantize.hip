@@ -175,7 +175,12 @@ void linear_quantize_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int T, int K, int H,
     int tiles_t, int tiles_n, int total, int grid, int xcd_grid, uint8_t *__restrict__ codes,
     uint16_t *__restrict__ s, uint16_t *__restrict__ z, uint16_t *__restrict__ y) {
-    static_assert(G >= 8 && G <= kSpanN && (G & (G - 1)) == 0, "group of 8..128 channels");
+    static_assert(G >= 8 && G <= kTileN && (G & (G - 1)) == 0, "group of 8..256 channels");
+    // a group of 256 channels is a whole tile row: the two waves that share
+    // its tokens (wn = 0, 1) each hold half of it and swap their halves'
+    // minimum and maximum through LDS
+    constexpr bool kSplitGroup = G > kSpanN;
+    constexpr int kGW = kSplitGroup ? kSpanN : G;    // channels of a group in one wave
     // Epilogue staging: a tile's codes (rows padded by 16 bytes to spread the
     // LDS banks), then its scales and zeros. When it fits between the first
     // pair buffer and the end of LDS (all but 8-bit codes in groups of 8), the
@@ -188,9 +193,12 @@ void linear_quantize_kernel(
     constexpr int kRingBytes = kPairs * kPair * 2;
     constexpr bool kEarly = kPair * 2 + kStagingBytes <= kLdsBytes;
     constexpr int kStagingOff = kEarly ? kPair * 2 : 0;
-    constexpr int kLdsUsed = kStagingOff + kStagingBytes > kRingBytes ? kStagingOff + kStagingBytes
-                                                                      : kRingBytes;
-    static_assert(kLdsUsed <= kLdsBytes && kStagingBytes <= kRingBytes, "staging fits in LDS");
+    // min/max swap area of split groups: per wave and token block, 32 (min, max) pairs
+    constexpr int kXchgOff = (kStagingOff + kStagingBytes + 15) / 16 * 16;
+    constexpr int kXchgBytes = kSplitGroup ? kThreads / kWave * kBlkT * 32 * 8 : 0;
+    constexpr int kLdsUsed = kXchgOff + kXchgBytes > kRingBytes ? kXchgOff + kXchgBytes : kRingBytes;
+    static_assert(kLdsUsed <= kLdsBytes && kStagingBytes + kXchgBytes <= kRingBytes,
+                  "staging fits in LDS");
     __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsUsed / 2];
 
     const uint32_t tid = __builtin_amdgcn_workitem_id_x();
@@ -446,11 +454,12 @@ void linear_quantize_kernel(
         // ---- epilogue: round to the dtype, quantize per (token, group) ----
         // Run j = 4 nb + m of a lane holds channels nb*32 + 8m + 4*(lane/32) + 0..3
         // of the wave's span (accumulator entries 4m..4m+3 of block nb); a group
-        // of G channels is RG = G/8 consecutive runs of each lane of the pair.
+        // of G channels is RG = G/8 consecutive runs of each lane of the pair
+        // (of 256 channels: the wave's 16 runs, and the partner wave's 16).
         // Codes, scales and zeros of the whole tile are first gathered in LDS
         // (kStagingOff) and then written out row by row in 16-byte pieces: a
         // token row of the tile is one contiguous run of codes.
-        constexpr int RG = G / 8;
+        constexpr int RG = kGW / 8;
         uint8_t *lc = reinterpret_cast<uint8_t *>(lds) + kStagingOff;
         uint8_t *lsz = lc + kTileT * kCodePitch;         // s rows, then z rows
         const int Hg = H / G;
@@ -467,7 +476,7 @@ void linear_quantize_kernel(
                                    (size_t)(n0 + wn * kSpanN)
                              : nullptr;
     #pragma unroll
-            for (int gi = 0; gi < kSpanN / G; ++gi) {
+            for (int gi = 0; gi < kSpanN / kGW; ++gi) {
                 // the group's values rounded to the dtype: packed pairs (yw) and
                 // widened back to binary32 (yv) -- what the layer would store
                 float yv[RG][4];
@@ -491,6 +500,19 @@ void linear_quantize_kernel(
                                                              __builtin_fmaxf(yv[jj][2], yv[jj][3])));
                 }
                 pair_minmax(mn, mx);
+                if constexpr (kSplitGroup) {
+                    // swap with the wave holding the other 128 channels of these tokens
+                    float *xc = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(lds) + kXchgOff) +
+                                (size_t)tb * (kThreads / kWave) * 64;
+                    if (fhalf == 0) {
+                        xc[(uint32_t)wave * 64u + frow * 2u] = mn;
+                        xc[(uint32_t)wave * 64u + frow * 2u + 1u] = mx;
+                    }
+                    wait_loads<63>();
+                    barrier_keep_loads();
+                    mn = __builtin_fminf(mn, xc[(uint32_t)(wave ^ 1) * 64u + frow * 2u]);
+                    mx = __builtin_fmaxf(mx, xc[(uint32_t)(wave ^ 1) * 64u + frow * 2u + 1u]);
+                }
                 const GroupParams p = group_params<BITS>(mn, mx);
     #pragma unroll
                 for (int jj = 0; jj < RG; ++jj) {
@@ -504,8 +526,8 @@ void linear_quantize_kernel(
                         *reinterpret_cast<uint16_t *>(lc + at) = (uint16_t)q;
                     if (yb && live) stv<u32x2, false>(yb, lane_y + ch * 2u, u32x2{yw[jj][0], yw[jj][1]});
                 }
-                if (fhalf == 0) {
-                    const uint32_t m = tl * kMetaRow + (uint32_t)(wn * (kSpanN / G) + gi) * 2u;
+                if (fhalf == 0 && (!kSplitGroup || wn == 0)) {
+                    const uint32_t m = tl * kMetaRow + (uint32_t)(wn * (kSpanN / kGW) + gi) * 2u;
                     *reinterpret_cast<uint16_t *>(lsz + m) = p.s16;
                     *reinterpret_cast<uint16_t *>(lsz + kTileT * kMetaRow + m) = p.z16;
                 }
@@ -539,16 +561,25 @@ void linear_quantize_kernel(
         FC_GLOBAL uint16_t *sg = sgpr_ptr(s + grow0 * (size_t)Hg + (size_t)(n0 / G));
         FC_GLOBAL uint16_t *zg = sgpr_ptr(z + grow0 * (size_t)Hg + (size_t)(n0 / G));
         const uint32_t mpitch = (uint32_t)Hg * 2u;
-        constexpr int kMetaWords = kMetaRow / 4;         // 4-byte pieces of a row
+        if constexpr (kMetaRow >= 4) {
+            constexpr int kMetaWords = kMetaRow / 4;     // 4-byte pieces of a row
     #pragma unroll
-        for (int i = 0; i < (kTileT * kMetaWords + kThreads - 1) / kThreads; ++i) {
-            const uint32_t id = (uint32_t)i * kThreads + wtid;
-            const uint32_t row = id / kMetaWords, c = id % kMetaWords;
-            if ((int)row < rows) {
-                const uint32_t at = row * kMetaRow + c * 4u;
-                stg<uint32_t>(sg, row * mpitch + c * 4u, *reinterpret_cast<const uint32_t *>(lsz + at));
-                stg<uint32_t>(zg, row * mpitch + c * 4u,
-                              *reinterpret_cast<const uint32_t *>(lsz + kTileT * kMetaRow + at));
+            for (int i = 0; i < (kTileT * kMetaWords + kThreads - 1) / kThreads; ++i) {
+                const uint32_t id = (uint32_t)i * kThreads + wtid;
+                const uint32_t row = id / kMetaWords, c = id % kMetaWords;
+                if ((int)row < rows) {
+                    const uint32_t at = row * kMetaRow + c * 4u;
+                    stg<uint32_t>(sg, row * mpitch + c * 4u, *reinterpret_cast<const uint32_t *>(lsz + at));
+                    stg<uint32_t>(zg, row * mpitch + c * 4u,
+                                  *reinterpret_cast<const uint32_t *>(lsz + kTileT * kMetaRow + at));
+                }
+            }
+        } else {
+            // one group per tile row: a 2-byte scale and zero per row
+            if ((int)wtid < rows) {
+                stg<uint16_t>(sg, wtid * mpitch, *reinterpret_cast<const uint16_t *>(lsz + wtid * 2u));
+                stg<uint16_t>(zg, wtid * mpitch,
+                              *reinterpret_cast<const uint16_t *>(lsz + kTileT * kMetaRow + wtid * 2u));
             }
         }
 
@@ -612,6 +643,7 @@ hipError_t by_group(const uint16_t *a, const uint16_t *w, int R, int T, int K, i
     case 32: return launch_one<DT, BITS, 32>(a, w, R, T, K, H, codes, s, z, y, stream);
     case 64: return launch_one<DT, BITS, 64>(a, w, R, T, K, H, codes, s, z, y, stream);
     case 128: return launch_one<DT, BITS, 128>(a, w, R, T, K, H, codes, s, z, y, stream);
+    case 256: return launch_one<DT, BITS, 256>(a, w, R, T, K, H, codes, s, z, y, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -176,7 +176,7 @@ fc_status fc_allreduce_emulated_residual(const void *x, fc_dtype dt, int R, int 
  * rounded product by the accumulation error; the codes are always those of
  * the y this call computes (and writes, when y != NULL).
  * Extra requirements (FC_ERR_SHAPE otherwise): K a positive multiple of 32
- * and at most 2^22, H a multiple of 256 and at most 2^24, group <= 128. Same
+ * and at most 2^22, H a multiple of 256 and at most 2^24, group <= 256. Same
  * checks as fc_quantize_groups otherwise; y, when given, 16-byte aligned.
  */
 fc_status fc_linear_quantize(const void *a, const void *w, fc_dtype dt, int R, int T, int K, int H,

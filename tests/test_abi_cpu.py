@@ -156,7 +156,7 @@ def test_other_entry_points_validate():
     LQ = L.fc_linear_quantize
     assert LQ(FAKE, FAKE, 1, 4, 8, 2000, 8192, 4, 128, FAKE, FAKE, FAKE, None, None) == 2  # K % 32
     assert LQ(FAKE, FAKE, 1, 4, 8, 2048, 8320, 4, 128, FAKE, FAKE, FAKE, None, None) == 2  # H % 256
-    assert LQ(FAKE, FAKE, 1, 4, 8, 2048, 8192, 4, 256, FAKE, FAKE, FAKE, None, None) == 2  # group
+    assert LQ(FAKE, FAKE, 1, 4, 8, 2048, 8192, 4, 512, FAKE, FAKE, FAKE, None, None) == 2  # group
     assert LQ(FAKE, FAKE, 1, 4, 8, 0, 8192, 4, 128, FAKE, FAKE, FAKE, None, None) == 2     # K = 0
     assert LQ(FAKE, FAKE, 1, 4, 8, (1 << 22) + 32, 8192, 4, 128, FAKE, FAKE, FAKE, None, None) == 2
     assert LQ(FAKE, FAKE, 1, 1, 8, 2048, (1 << 24) + 256, 4, 128, FAKE, FAKE, FAKE, None, None) == 2

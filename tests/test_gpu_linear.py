@@ -93,6 +93,9 @@ EXACT = [  # (R, T, K, H, group, bits, dtype)
     (3, 1024, 3104, 768, 128, 8, oracle.F16),   # K >= 3072 but 3 channel tiles: XCD runs; odd stage count
     (2, 300, 352, 512, 8, 4, oracle.F16),       # 4-bit codes in groups of 8 (staging loads in one burst), 11 stages
     (1, 700, 160, 256, 8, 4, oracle.BF16),      # the same, bf16, 5 stages
+    (2, 300, 160, 512, 256, 4, oracle.BF16),    # groups of 256: a tile row, split over two waves
+    (1, 257, 64, 256, 256, 8, oracle.F16),      # the same, one channel tile, INT8
+    (2, 2048, 3072, 512, 256, 4, oracle.F16),   # the same on the XCD grid
 ]
 
 
@@ -115,14 +118,14 @@ def test_dyadic_inputs_bit_exact(R, T, K, H, group, bits, dtype):
 def _draw_linear(rng):
     """A supported (R, T, K, H, group, bits, dtype): K a multiple of 32 (odd
     stage counts included: the last staged pair is then half used), H a
-    multiple of 256 and of R, group <= 128; sizes kept small."""
+    multiple of 256 and of R, group <= 256; sizes kept small."""
     R = int(rng.integers(1, 5))
     K = 32 * int(rng.integers(1, 24))
     H = 256 * int(rng.integers(1, 5))
     if H % R:
         H *= R                                   # H % R == 0 (the chunking needs it)
     T = int(rng.integers(1, 600))
-    group = int(2 ** rng.integers(3, 8))
+    group = int(2 ** rng.integers(3, 9))
     bits = int(rng.choice([4, 8]))
     dtype = oracle.F16 if rng.random() < 0.5 else oracle.BF16
     return R, T, K, H, group, bits, dtype
