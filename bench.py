@@ -425,7 +425,7 @@ def main() -> int:
         linear = {}
         shapes = [("o_proj", H // R)] + ([("d_proj", w.ffn // R)] if w.ffn else [])
         for name, Kl in shapes:
-            if Kl % 32 or H % 256 or group > 128:
+            if Kl % 32 or H % 256 or group > 256:
                 continue
             gen = torch.Generator(device=dev).manual_seed(args.seed)
             la = torch.randn((R, T, Kl), generator=gen, device=dev, dtype=torch.float32).to(tdt)
