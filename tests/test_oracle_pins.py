@@ -276,6 +276,73 @@ def test_stage2_groups_are_min_of_group_and_chunk():
             assert _hval(res["z2"][t, j]) == float(np.float16(mn))
 
 
+def _fixture_group(name: str):
+    fx = _read_fixture(name)
+    bits, group = int(fx["bits"][0]), int(fx["group"][0])
+    x = _f16([float(v) for v in fx["x"]]).reshape(1, 1, -1)
+    codes1, s1, z1 = oracle.quantize_groups(x, oracle.F16, bits, group)
+    return fx, bits, codes1, s1, z1
+
+
+def test_codes_use_the_binary32_reciprocal_not_a_divide():
+    """One element is an exact half step of (x - z)/s but not of fp32(x - z) * fp32(1/s):
+    the pinned reading (one reciprocal per group) gives 15 where a divide gives 14."""
+    fx, bits, codes1, s1, z1 = _fixture_group("recip_vs_divide_int4_g8_f16.txt")
+    assert int(s1[0, 0, 0]) == int(fx["s_bits"][0], 16)
+    assert int(z1[0, 0, 0]) == int(fx["z_bits"][0], 16)
+    got = list(_unpack(codes1, bits)[0, 0])
+    assert got == [int(v) for v in fx["codes"]]
+    assert got != [int(v) for v in fx["codes_if_divided"]]
+    assert list(codes1[0, 0]) == [int(v, 16) for v in fx["packed"]]
+
+
+def test_codes_take_two_binary32_roundings():
+    """t = fp32(fp32(x - z) * inv): six exact half steps round to the even codes, where one
+    fused multiply-add on the distributed form x*inv - z*inv rounds them to the odd ones."""
+    fx, bits, codes1, s1, z1 = _fixture_group("two_roundings_int4_g8_f16.txt")
+    assert int(s1[0, 0, 0]) == int(fx["s_bits"][0], 16)
+    assert int(z1[0, 0, 0]) == int(fx["z_bits"][0], 16)
+    got = list(_unpack(codes1, bits)[0, 0])
+    assert got == [int(v) for v in fx["codes"]]
+    assert got != [int(v) for v in fx["codes_if_fused"]]
+    assert list(codes1[0, 0]) == [int(v, 16) for v in fx["packed"]]
+
+
+def test_stage2_zero_point_below_the_minimum():
+    """A stage-2 group whose minimum sum is a tie in fp16 that rounds below it: z2 lies
+    under the group, the top code clamps at Q, and that element's error is a whole scale
+    step -- over s/2, within s/2 + |z - min|. The other chunk is reproduced exactly."""
+    fx = _read_fixture("stage2_zero_below_min_r2_int4.txt")
+    bits, group = int(fx["bits"][0]), int(fx["group"][0])
+    x = np.stack([_f16([float(v) for v in fx["x0"]]), _f16([float(v) for v in fx["x1"]])])
+    x = x.reshape(2, 1, -1)
+    res = oracle.allreduce(x, oracle.F16, bits, group)
+    hexes = lambda k: [int(v, 16) for v in fx[k]]
+    assert list(res["s1"][0, 0]) == hexes("s1_bits_r0")
+    assert list(res["z1"][0, 0]) == hexes("z1_bits_r0")
+    assert list(res["s1"][1, 0]) == hexes("s1_bits_r1")
+    assert list(res["z1"][1, 0]) == hexes("z1_bits_r1")
+    assert list(_unpack(res["codes1"], bits)[1, 0]) == [int(v) for v in fx["codes1_r1"]]
+    assert not _unpack(res["codes1"], bits)[0].any()
+    y = res["y"][0].astype(np.float64)
+    assert list(y) == [float(v) for v in fx["y"]]
+    assert res["group2"] == 8
+    assert list(res["s2"][0]) == hexes("s2_bits")
+    assert list(res["z2"][0]) == hexes("z2_bits")
+    assert list(_unpack(res["codes2"], bits)[0]) == [int(v) for v in fx["codes2"]]
+    assert list(res["codes2"][0]) == hexes("packed2")
+    o32 = res["o32"][0].astype(np.float64)
+    assert list(o32) == [float(v) for v in fx["o32"]]
+    assert list(_hval(res["out"][0])) == [float(v) for v in fx["out_f16"]]
+    s2 = _hval(res["s2"][0])
+    z2 = _hval(res["z2"][0])
+    err = np.abs(o32 - y).reshape(2, 8).max(axis=1)
+    mn = y.reshape(2, 8).min(axis=1)
+    assert err[0] == s2[0] > s2[0] / 2          # the clamp: more than half a scale
+    assert err[0] <= s2[0] / 2 + abs(z2[0] - mn[0])
+    assert err[1] == 0.0
+
+
 # ---------------------------------------------------------------------------
 # brute force: the code is the nearest grid point
 # ---------------------------------------------------------------------------
@@ -343,7 +410,10 @@ def _widen(bits: np.ndarray, dtype: str) -> np.ndarray:
 
 @pytest.mark.parametrize("name", _BOUND_CASES)
 def test_per_stage_error_at_most_half_scale(name):
-    """|x_hat - x| <= s*(1/2 + 2^-14) + 2^-23*|x| + max(0, z - mn) per stage (normal scales)."""
+    """|x_hat - x| <= s*(1/2 + 2^-14) + 2^-23*|x| + |z - mn| per stage (normal scales).
+    The last term is the distance of the fp16 zero point from the group minimum: 0 for
+    fp16 stage-1 input, up to half an fp16 spacing of |mn| for binary32 stage-2 sums,
+    where a zero below the minimum clamps the top codes at Q."""
     w = _small(name, T=16)
     x = synth.operands(w, 0)
     res = oracle.allreduce(x, w.dtype, w.bits, w.group)
@@ -356,7 +426,7 @@ def test_per_stage_error_at_most_half_scale(name):
     z1 = _hval(res["z1"])[..., None]
     xh = (q1 * s1 + z1).astype(np.float32).astype(np.float64)
     mn = xv.min(axis=-1, keepdims=True)
-    bound = s1 * (0.5 + 2.0 ** -14) + 2.0 ** -23 * np.abs(xv) + np.maximum(0, z1 - mn)
+    bound = s1 * (0.5 + 2.0 ** -14) + 2.0 ** -23 * np.abs(xv) + np.abs(z1 - mn)
     normal = s1 >= 2.0 ** -14
     assert np.all((np.abs(xh - xv) <= bound) | ~normal)
     # stage 2 against its own input y
@@ -365,8 +435,29 @@ def test_per_stage_error_at_most_half_scale(name):
     s2 = _hval(res["s2"])[..., None]
     z2 = _hval(res["z2"])[..., None]
     mn2 = y.min(axis=-1, keepdims=True)
-    bound2 = s2 * (0.5 + 2.0 ** -14) + 2.0 ** -23 * np.abs(y) + np.maximum(0, z2 - mn2)
+    bound2 = s2 * (0.5 + 2.0 ** -14) + 2.0 ** -23 * np.abs(y) + np.abs(z2 - mn2)
     assert np.all((np.abs(o - y) <= bound2) | ~(s2 >= 2.0 ** -14))
+
+
+def test_stage2_bound_needs_the_zero_point_term():
+    """Groups with a large offset and a small range (R = 2, fp16, 4-bit codes, groups of 32):
+    the stage-2 error stays within s/2 + |z - mn| everywhere, and the |z - mn| term is
+    needed -- without it the bound fails where the fp16 zero rounds below the minimum sum."""
+    rng = np.random.default_rng(11)
+    R, T, H, g = 2, 16, 256, 32
+    off = rng.uniform(-60, -35, size=(1, T, H // g, 1))
+    v = off / R + rng.uniform(-0.02, 0.02, size=(R, T, H // g, g))
+    x = v.reshape(R, T, H).astype(np.float16).view(np.uint16)
+    res = oracle.allreduce(x, oracle.F16, 4, g)
+    y = res["y"].astype(np.float64).reshape(T, H // g, g)
+    o = res["o32"].astype(np.float64).reshape(T, H // g, g)
+    s2 = _hval(res["s2"])[..., None]
+    z2 = _hval(res["z2"])[..., None]
+    mn2 = y.min(axis=-1, keepdims=True)
+    err = np.abs(o - y)
+    half = s2 * (0.5 + 2.0 ** -14) + 2.0 ** -23 * np.abs(y)
+    assert np.all(err <= half + np.abs(z2 - mn2))
+    assert np.any(err > half)
 
 
 @pytest.mark.parametrize("name", _BOUND_CASES)
