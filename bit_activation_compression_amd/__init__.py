@@ -25,6 +25,7 @@ __all__ = [
     "fc_quantize_groups", "fc_dequant_sum_requant", "fc_dequantize", "fc_allreduce_emulated",
     "fc_workspace_bytes", "fc_workspace_layout", "fc_stage2_group", "fc_status_string",
     "fc_sum_uncompressed", "fc_dequantize_residual", "fc_linear_quantize", "workspace_views",
+    "fc_allreduce_emulated_noalloc", "NOALLOC_SCRATCH_BYTES",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -39,7 +40,10 @@ EXPORTED_SYMBOLS = (
     "fc_sum_uncompressed", "fc_dequant_sum_requant_mixed", "fc_allreduce_emulated_mixed",
     "fc_workspace_bytes_mixed", "fc_workspace_layout_mixed",
     "fc_dequantize_residual", "fc_allreduce_emulated_residual", "fc_linear_quantize",
+    "fc_allreduce_emulated_noalloc",
 )
+# FC_NOALLOC_SCRATCH_BYTES of include/fc.h: the payload scratch the library holds per device
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lock = threading.Lock()
 _lib = None
@@ -72,10 +76,12 @@ def lib() -> ctypes.CDLL:
             L.fc_dequantize_residual.argtypes = [P, P, P, I, I, I, I, I, P, P, P]
             L.fc_allreduce_emulated_residual.argtypes = [P, I, I, I, I, I, I, I, P, P, P, Z, P]
             L.fc_linear_quantize.argtypes = [P, P, I, I, I, I, I, I, I, P, P, P, P, P]
+            L.fc_allreduce_emulated_noalloc.argtypes = [P, I, I, I, I, I, I, P, P]
             for f in (L.fc_linear_quantize, L.fc_quantize_groups, L.fc_dequant_sum_requant, L.fc_dequantize,
                       L.fc_allreduce_emulated, L.fc_sum_uncompressed,
                       L.fc_dequant_sum_requant_mixed, L.fc_allreduce_emulated_mixed,
-                      L.fc_dequantize_residual, L.fc_allreduce_emulated_residual):
+                      L.fc_dequantize_residual, L.fc_allreduce_emulated_residual,
+                      L.fc_allreduce_emulated_noalloc):
                 f.restype = I
             L.fc_workspace_bytes_mixed.argtypes = [I, I, I, I, I, I]
             L.fc_workspace_bytes_mixed.restype = Z
@@ -327,6 +333,26 @@ def fc_allreduce_emulated(x: torch.Tensor, bits: int, group: int, out=None, work
                                                _stream(stream, dev))
     _check(st, "fc_allreduce_emulated")
     return out, workspace
+
+
+def fc_allreduce_emulated_noalloc(x: torch.Tensor, bits: int, group: int, out=None,
+                                  stream=None):
+    """x [R, T, H] -> out [T, H]: fc_allreduce_emulated with both payloads in the library's
+    own per-device scratch (the C call allocates nothing; pass `out` to allocate nothing
+    here either). Raises FcError (FC_ERR_SCRATCH) when the payloads exceed
+    NOALLOC_SCRATCH_BYTES. Calls that overlap in time on one device race on the scratch."""
+    _dev_tensor(x, "x")
+    R, T, H = x.shape
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=dev)
+    if out.dtype != x.dtype:
+        raise ValueError("out must have x's dtype")
+    _room(out, "out", T * H * 2, dev)
+    _check(lib().fc_allreduce_emulated_noalloc(_ptr(x), _dt(x, "x"), R, T, H, bits, group,
+                                               _ptr(out), _stream(stream, dev)),
+           "fc_allreduce_emulated_noalloc")
+    return out
 
 
 def fc_sum_uncompressed(x: torch.Tensor, out=None, stream=None):

@@ -3,6 +3,7 @@
 // enqueued, and nothing here calls the HIP runtime until the launches.
 #include <stdint.h>
 
+#include <atomic>
 #include <initializer_list>
 
 #include "fc.h"
@@ -130,6 +131,31 @@ fc_status allreduce_emulated(const void *x, fc_dtype dt, int R, int T, int H, in
                                           static_cast<uint16_t *>(out), s));
 }
 
+// Payload scratch of fc_allreduce_emulated_noalloc: one array per device
+// (each device that loads the library holds its own copy until the process
+// ends). In host code the name is only a host-side stand-in, never a device
+// address: the device address comes from noalloc_scratch().
+static __device__ __align__(256) uint8_t scratch[FC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of the current device's scratch array, looked up with
+// hipGetSymbolAddress on the first call on that device and cached per device
+// (atomic: host threads racing on a first call store the same address).
+// nullptr if the runtime reports an error.
+void *noalloc_scratch() {
+    static std::atomic<void *> cached[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = cached[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return nullptr;
+        cached[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -217,6 +243,23 @@ fc_status fc_allreduce_emulated(const void *x, fc_dtype dt, int R, int T, int H,
                                        workspace_bytes, stream);
 }
 
+fc_status fc_allreduce_emulated_noalloc(const void *x, fc_dtype dt, int R, int T, int H, int bits,
+                                        int group, void *out, void *stream) {
+    int g2 = 0;
+    fc_status st = check_shape(R, T, H, bits, group, &g2);
+    if (st != FC_OK) return st;
+    if (dt != FC_F16 && dt != FC_BF16) return FC_ERR_DTYPE;
+    const uint64_t n = (uint64_t)T * (uint64_t)H;
+    st = check_ptrs(n, {x, out});
+    if (st != FC_OK || n == 0) return st;
+    if (layout(R, T, H, bits, bits, group, g2).total > FC_NOALLOC_SCRATCH_BYTES)
+        return FC_ERR_SCRATCH;
+    void *ws = noalloc_scratch();
+    if (ws == nullptr) return FC_ERR_LAUNCH;
+    return allreduce_emulated(x, dt, R, T, H, bits, bits, group, false, nullptr, out, ws,
+                              FC_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 fc_status fc_sum_uncompressed(const void *x, fc_dtype dt, int R, int T, int H, void *out,
                               void *stream) {
     if (R < 1 || T < 0 || H < 1 || H % 8 != 0) return FC_ERR_SHAPE;
@@ -295,6 +338,8 @@ const char *fc_status_string(fc_status s) {
     case FC_ERR_WORKSPACE: return "FC_ERR_WORKSPACE: workspace smaller than fc_workspace_bytes()";
     case FC_ERR_LAUNCH: return "FC_ERR_LAUNCH: the HIP runtime reported a launch error";
     case FC_ERR_DTYPE: return "FC_ERR_DTYPE: dtype must be FC_F16 or FC_BF16";
+    case FC_ERR_SCRATCH:
+        return "FC_ERR_SCRATCH: the payloads exceed the library's scratch (FC_NOALLOC_SCRATCH_BYTES)";
     }
     return "unknown fc_status";
 }

@@ -39,7 +39,10 @@
  *     (|min| > 65504 or (max - min)/Q > 65504), are outside the contract:
  *     the results are unspecified but every access stays in bounds.
  *   - No global state beyond a per-device cache of the compute-unit count
- *     (atomic): concurrent calls on different streams are safe.
+ *     (atomic) and the payload scratch of fc_allreduce_emulated_noalloc
+ *     (one array per device, with its cached address): concurrent calls on
+ *     different streams are safe, except overlapping calls of
+ *     fc_allreduce_emulated_noalloc on one device.
  *
  * Supported shapes (FC_ERR_SHAPE otherwise): R >= 1, T >= 0, H >= 1,
  * bits in {4, 8} (FC_ERR_BITS), group a power of two in [8, 8192] dividing H,
@@ -64,7 +67,8 @@ typedef enum {
     FC_ERR_ALIGN = 4,      /* a device pointer is not 16-byte aligned */
     FC_ERR_WORKSPACE = 5,  /* workspace smaller than fc_workspace_bytes() */
     FC_ERR_LAUNCH = 6,     /* the HIP runtime reported an error at launch */
-    FC_ERR_DTYPE = 7       /* dtype is not FC_F16 or FC_BF16 */
+    FC_ERR_DTYPE = 7,      /* dtype is not FC_F16 or FC_BF16 */
+    FC_ERR_SCRATCH = 8     /* the payloads exceed FC_NOALLOC_SCRATCH_BYTES */
 } fc_status;
 
 typedef enum { FC_F16 = 0, FC_BF16 = 1 } fc_dtype;
@@ -182,6 +186,28 @@ fc_status fc_allreduce_emulated_residual(const void *x, fc_dtype dt, int R, int 
 fc_status fc_linear_quantize(const void *a, const void *w, fc_dtype dt, int R, int T, int K, int H,
                              int bits, int group, uint8_t *codes1, uint16_t *s1, uint16_t *z1,
                              void *y, void *stream);
+
+/*
+ * fc_allreduce_emulated for callers that cannot allocate device memory at all
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same result, bit for bit, with both payloads kept in a
+ * scratch array that the library itself holds on each device it runs on, of
+ * FC_NOALLOC_SCRATCH_BYTES, for as long as the process lives. Nothing is
+ * allocated per call (no hipMalloc, hipFree or allocating library routine).
+ *   x [R][T][H] in dt  ->  out [T][H] in dt; the caller passes both.
+ * Returns FC_ERR_SCRATCH, before enqueueing anything, when
+ * fc_workspace_bytes(R, T, H, bits, group) exceeds FC_NOALLOC_SCRATCH_BYTES.
+ * Every call on one device uses that device's one array; no part of it has to
+ * start at zero (each payload byte a call reads, the same call wrote first),
+ * but calls that overlap in time on one device -- on different streams, or
+ * from different host threads without ordering -- race on it and their
+ * results are then undefined. Calls on one stream are ordered and safe.
+ * The array's device address is looked up once per device (first call there).
+ */
+#define FC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+fc_status fc_allreduce_emulated_noalloc(const void *x, fc_dtype dt, int R, int T, int H, int bits,
+                                        int group, void *out, void *stream);
 
 /* Workspace size and layout for the mixed-width pipeline (same slice order). */
 size_t fc_workspace_bytes_mixed(int R, int T, int H, int bits1, int bits2, int group);

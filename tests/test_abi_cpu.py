@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     L = fc.lib()
     names = _declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
     assert sorted(names) == sorted(fc.EXPORTED_SYMBOLS)
@@ -48,7 +48,7 @@ def test_no_kernel_launch_stub_left_undefined():
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(9):
         assert fc.fc_status_string(s).startswith("FC_")
     assert "unknown" in fc.fc_status_string(99)
 
@@ -165,3 +165,24 @@ def test_other_entry_points_validate():
     assert LQ(FAKE, None, 1, 4, 8, 2048, 8192, 4, 128, FAKE, FAKE, FAKE, None, None) == 1
     assert LQ(FAKE, FAKE, 1, 4, 8, 2048, 8192, 4, 128, FAKE, FAKE, FAKE, MISALIGNED, None) == 4
     assert LQ(None, None, 1, 4, 0, 2048, 8192, 4, 128, None, None, None, None, None) == 0
+
+
+def test_noalloc_entry_point_validates_before_any_runtime_call():
+    L = fc.lib()
+    NA = L.fc_allreduce_emulated_noalloc
+    assert NA(FAKE, 0, 3, 8, 256, 4, 128, FAKE, None) == 2          # H % R
+    assert NA(FAKE, 0, 2, 8, 256, 4, 96, FAKE, None) == 2           # group
+    assert NA(FAKE, 0, 2, 8, 256, 6, 128, FAKE, None) == 3          # bits
+    assert NA(FAKE, 2, 2, 8, 256, 4, 128, FAKE, None) == 7          # dtype
+    assert NA(FAKE, 0, 2, 8, 256, 4, 128, None, None) == 1
+    assert NA(MISALIGNED, 0, 2, 8, 256, 4, 128, FAKE, None) == 4
+    assert NA(None, 0, 2, 0, 256, 4, 128, None, None) == 0          # T == 0
+    # payloads larger than the library's fixed scratch: rejected, nothing enqueued
+    assert fc.fc_workspace_bytes(4, 8192, 8192, 4, 128) > fc.NOALLOC_SCRATCH_BYTES
+    assert NA(FAKE, 1, 4, 8192, 8192, 4, 128, FAKE, None) == 8
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define FC_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == fc.NOALLOC_SCRATCH_BYTES
