@@ -16,12 +16,25 @@ Metric: algorithmic HBM bytes per step / time per step (GB/s). Algorithmic
 bytes: every input read once, each payload written once and read once, the
 output written once (scales and zeros 4 bytes per group).
 
-Prints one JSON line. `roofline` is for K1, the kernel that moves two thirds
-of the bytes, timed with HIP events on the stream it runs on.
+Order of a run:
+  1. settle: pipeline steps back to back until the time per step is steady
+     (after idle, the GPU's power management holds the engine clock down for
+     the first ~15 ms of load; the path's steady state is what is measured);
+  2. W warm-up steps, then exactly K timed steps with no event in the stream
+     (the timed region is bracketed by device synchronizations only);
+  3. a separate pass of 50 steps with HIP events around each kernel, on the
+     same stream: per-kernel times and K1's roofline (K1 moves two thirds of
+     the bytes);
+  4. the same K steps after an idle second (the cold-start figure);
+  5. the other workloads (LLaMA-3-8B prefill, the group-size sweep with its
+     errors, decode latency, tiny), the streaming ceilings, the uncompressed
+     comparator, the residual-add and linear-layer fusions, the CPU oracle.
+Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -42,11 +55,22 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_llama3_70b_prefill_traff
 K1_SOURCES = ("bit_activation_compression_amd/csrc/fc_quantize.hip",
               "bit_activation_compression_amd/csrc/fc_device.h")
 
+BREAKDOWN_STEPS = 50   # steps of the per-kernel event pass
+GRAPH_CALLS = 20       # calls captured per HIP graph in the launch-bound measurements
+LINEAR_ROUNDS = 3      # interleaved timing rounds of the linear-layer variants
+CPU_PASSES = 3         # passes of the CPU oracle over the whole workload (~4-5 s each)
+SETTLE_MIN_MS = 60.0   # least back-to-back time before the clock is taken as steady
+SETTLE_MAX_MS = 800.0
+SETTLE_BLOCK_MS = 6.0
+COLD_IDLE_S = 1.0
 
-def model_bytes(R: int, T: int, H: int, bits: int, group: int, group2: int, e: int = 2) -> dict:
+
+def model_bytes(R: int, T: int, H: int, bits: int, group: int, group2: int, e: int = 2,
+                bits2: int | None = None) -> dict:
+    bits2 = bits if bits2 is None else bits2
     n1, n2 = R * T * H, T * H
     p1 = n1 * bits // 8 + n1 // group * 4
-    p2 = n2 * bits // 8 + n2 // group2 * 4
+    p2 = n2 * bits2 // 8 + n2 // group2 * 4
     k1 = n1 * e + p1
     k2 = p1 + p2
     k3 = p2 + n2 * e
@@ -62,19 +86,6 @@ def link_bytes(R: int, T: int, H: int, bits: int, group: int, group2: int, e: in
         else (R - 1) * (T * (H // R) * bits // 8 + T * (H // group) * 4)
     ag = (R - 1) * (T * (H // R) * bits // 8 + T * (H // R) // group2 * 4)
     return {"ring_16bit": ring, "two_step_codec": rs + ag, "ratio": round(ring / (rs + ag), 3)}
-
-
-K1_SAMPLE_EVERY = 10
-GRAPH_CALLS = 20       # calls captured per HIP graph in the launch-bound measurements
-LINEAR_ROUNDS = 3      # interleaved timing rounds of the linear-layer variants
-CPU_PASSES = 3         # passes of the CPU oracle over the whole workload (~4-5 s each)
-
-
-def k1_sample_every(steps: int) -> int:
-    """Stride of the timed steps whose K1 launch is bracketed by HIP events:
-    every K1_SAMPLE_EVERY-th step, closer when that would leave fewer than 20
-    samples, every step for short runs."""
-    return max(1, min(K1_SAMPLE_EVERY, steps // 20))
 
 
 def code_only(src: str) -> str:
@@ -97,8 +108,9 @@ def k1_source_hash() -> str:
 
 
 def measured_traffic(workload: str) -> float | None:
-    """HBM bytes per K1 launch from the committed rocprofv3 counter summary, if it
-    was taken on this workload and on the current K1 source; None otherwise."""
+    """L2-to-fabric bytes per K1 launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size), if it was taken on this
+    workload and on the current K1 source; None otherwise."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     txt = open(TRAFFIC_FILE).read()
@@ -112,15 +124,107 @@ def measured_traffic(workload: str) -> float | None:
     return float(m_b.group(1))
 
 
-def cpu_model() -> str:
+def host_info() -> dict:
+    """The host the CPU oracle ran on: /proc/cpuinfo fields, logical CPUs in the machine
+    and in this process's affinity set."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if info:
+                        break
+                    continue
+                k, v = (p.strip() for p in line.split(":", 1))
+                if k in ("vendor_id", "model name", "cpu family", "model", "stepping", "cpu MHz",
+                         "cache size") and k not in info:
+                    info[k] = v
     except OSError:
         pass
-    return platform.processor() or "unknown"
+    info["host_nproc"] = os.cpu_count()
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    info["platform"] = platform.platform()
+    return info
+
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def settle_clock(torch, fn, stream, min_ms=SETTLE_MIN_MS, max_ms=SETTLE_MAX_MS) -> dict:
+    """Run fn() back to back until the time per call is steady: blocks of ~SETTLE_BLOCK_MS,
+    each bracketed by events (between blocks only), until at least min_ms have passed and two
+    consecutive blocks agree within 1% (or max_ms is reached)."""
+    for _ in range(3):
+        fn()
+    e = _events(torch, 2)
+    e[0].record(stream)
+    for _ in range(3):
+        fn()
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    per = max(e[0].elapsed_time(e[1]) / 3, 1e-3)
+    block = max(1, int(round(SETTLE_BLOCK_MS / per)))
+    times, total, calls = [], 0.0, 6
+    while True:
+        e = _events(torch, 2)
+        e[0].record(stream)
+        for _ in range(block):
+            fn()
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        ms = e[0].elapsed_time(e[1])
+        total += ms
+        calls += block
+        times.append(ms / block)
+        if total >= min_ms and len(times) >= 2 and abs(times[-1] - times[-2]) <= 0.01 * times[-2]:
+            steady = True
+            break
+        if total >= max_ms:
+            steady = False
+            break
+    return {"calls": calls, "ms": round(total, 2), "steady": steady,
+            "first_block_ms_per_call": round(times[0], 5), "last_block_ms_per_call": round(times[-1], 5)}
+
+
+def timed_calls(torch, fn, stream, n) -> float:
+    """ms per call of n back-to-back calls, events around the whole run."""
+    e = _events(torch, 2)
+    e[0].record(stream)
+    for _ in range(n):
+        fn()
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    return e[0].elapsed_time(e[1]) / n
+
+
+def stage_errors(torch, fc, xf, out, ws, R, T, H, bits, bits2, g, g2) -> dict:
+    """Per-element MSE of each stage, from the payloads the library wrote (torch on the GPU):
+      stage1_mse: mean over r, t, h of (dequantized payload 1 - x)^2
+      stage2_mse: mean of (dequantized payload 2 - sum_r dequantized payload 1)^2
+      total_mse : mean of (output - sum_r x)^2, the sum in binary32."""
+    v = fc.workspace_views(ws, R, T, H, bits, g, bits2=bits2)
+    s1 = v["s1"].view(torch.float16).float().repeat_interleave(g, dim=2)
+    z1 = v["z1"].view(torch.float16).float().repeat_interleave(g, dim=2)
+    c1 = v["codes1"]
+    q1 = torch.stack([c1 & 15, c1 >> 4], dim=-1).reshape(R, T, H) if bits == 4 else c1
+    xh32 = q1.float() * s1 + z1
+    y = xh32[0].clone()
+    for r in range(1, R):
+        y = y + xh32[r]
+    s2 = v["s2"].view(torch.float16).float().repeat_interleave(g2, dim=1)
+    z2 = v["z2"].view(torch.float16).float().repeat_interleave(g2, dim=1)
+    c2 = v["codes2"]
+    q2 = torch.stack([c2 & 15, c2 >> 4], dim=-1).reshape(T, H) if bits2 == 4 else c2
+    yh = q2.float() * s2 + z2
+    exact = xf.sum(dim=0)
+    return {"stage1_mse": float(((xh32 - xf) ** 2).mean()),
+            "stage2_mse": float(((yh - y) ** 2).mean()),
+            "total_mse": float(((out.float() - exact) ** 2).mean()),
+            "exact_sum_power": float((exact ** 2).mean())}
 
 
 def quality_report(seed: int) -> int:
@@ -129,11 +233,7 @@ def quality_report(seed: int) -> int:
     Reduce-Scatter vs before the All-Gather), on the synthetic operands; plus throughput.
     The codec runs in the library's kernels; the error statistics (and the binary32
     dequantized values they need) are computed with torch on the GPU from the payloads
-    the library wrote.
-      stage1_mse: mean over r, t, h of (dequantized payload 1 - x)^2
-      stage2_mse: mean of (dequantized payload 2 - sum_r dequantized payload 1)^2
-      total_mse : mean of (output - sum_r x)^2
-    Prints one JSON line with a record per configuration."""
+    the library wrote. Prints one JSON line with a record per configuration."""
     import numpy as np
     import torch
 
@@ -155,77 +255,183 @@ def quality_report(seed: int) -> int:
         x_host = synth.operands(w, seed)
         xd = torch.from_numpy(x_host.view(np.int16)).to(dev).view(tdt)
         xf = xd.float()
-        exact = xf.sum(dim=0)
         for bits, bits2 in widths[name]:
             g2 = fc.fc_stage2_group(R, H, g)
             out, ws = fc.fc_allreduce_emulated(xd, bits, g, bits2=bits2)
-            v = fc.workspace_views(ws, R, T, H, bits, g, bits2=bits2)
-            # the dequantized stage values in binary32, as the receiver sums them
-            s1 = v["s1"].view(torch.float16).float().repeat_interleave(g, dim=2)
-            z1 = v["z1"].view(torch.float16).float().repeat_interleave(g, dim=2)
-            c1 = v["codes1"]
-            q1 = torch.stack([c1 & 15, c1 >> 4], dim=-1).reshape(R, T, H) if bits == 4 else c1
-            xh32 = q1.float() * s1 + z1
-            y = xh32[0].clone()
-            for r in range(1, R):
-                y = y + xh32[r]
-            s2 = v["s2"].view(torch.float16).float().repeat_interleave(g2, dim=1)
-            z2 = v["z2"].view(torch.float16).float().repeat_interleave(g2, dim=1)
-            c2 = v["codes2"]
-            q2 = torch.stack([c2 & 15, c2 >> 4], dim=-1).reshape(T, H) if bits2 == 4 else c2
-            yh = q2.float() * s2 + z2
-            rec = {"workload": name, "bits_rs": bits, "bits_ag": bits2, "group": g, "group2": g2,
-                   "stage1_mse": float(((xh32 - xf) ** 2).mean()),
-                   "stage2_mse": float(((yh - y) ** 2).mean()),
-                   "total_mse": float(((out.float() - exact) ** 2).mean()),
-                   "exact_sum_power": float((exact ** 2).mean())}
-            del s1, z1, q1, xh32, y, s2, z2, q2, yh
-            # throughput of the whole path on this configuration
-            for _ in range(5):
+            rec = {"workload": name, "bits_rs": bits, "bits_ag": bits2, "group": g, "group2": g2}
+            rec.update(stage_errors(torch, fc, xf, out, ws, R, T, H, bits, bits2, g, g2))
+
+            def call():
                 fc.fc_allreduce_emulated(xd, bits, g, out, ws, stream=stream, bits2=bits2)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            ev[0].record(stream)
-            for _ in range(20):
-                fc.fc_allreduce_emulated(xd, bits, g, out, ws, stream=stream, bits2=bits2)
-            ev[1].record(stream)
-            torch.cuda.synchronize()
-            ms = ev[0].elapsed_time(ev[1]) / 20
-            n1, n2 = R * T * H, T * H
-            p1 = n1 * bits // 8 + n1 // g * 4
-            p2 = n2 * bits2 // 8 + n2 // g2 * 4
-            total = n1 * 2 + 2 * p1 + 2 * p2 + n2 * 2
+
+            settle_clock(torch, call, stream, min_ms=30.0)
+            ms = timed_calls(torch, call, stream, 20)
+            total = model_bytes(R, T, H, bits, g, g2, bits2=bits2)["total"]
             rec.update({"us_per_call": round(ms * 1e3, 2), "gbps": round(total / (ms * 1e-3) / 1e9, 1)})
-            if T * H <= 1 << 20:
-                # launch-bound shapes: GRAPH_CALLS consecutive calls captured in one
-                # HIP graph (as a serving step would be) and replayed; per-call time
-                graph = torch.cuda.CUDAGraph()
-                cap = torch.cuda.Stream(dev)
-                cap.wait_stream(stream)
-                with torch.cuda.stream(cap):
-                    fc.fc_allreduce_emulated(xd, bits, g, out, ws, stream=cap, bits2=bits2)
-                    with torch.cuda.graph(graph, stream=cap):
-                        for _ in range(GRAPH_CALLS):
-                            fc.fc_allreduce_emulated(xd, bits, g, out, ws, stream=cap, bits2=bits2)
-                stream.wait_stream(cap)
-                torch.cuda.synchronize()
-                for _ in range(3):
-                    graph.replay()
-                ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-                ev[0].record(stream)
-                for _ in range(10):
-                    graph.replay()
-                ev[1].record(stream)
-                torch.cuda.synchronize()
-                rec["us_per_call_graph"] = round(ev[0].elapsed_time(ev[1]) / (10 * GRAPH_CALLS) * 1e3, 2)
-                rec["graph_calls_per_replay"] = GRAPH_CALLS
-                del graph
             records.append(rec)
             print(f"[quality] {name} int{bits}->int{bits2}: stage1 {rec['stage1_mse']:.4g} "
                   f"stage2 {rec['stage2_mse']:.4g} total {rec['total_mse']:.4g} "
                   f"{rec['us_per_call']} us {rec['gbps']} GB/s", file=sys.stderr, flush=True)
-        del xd, xf, exact
+        del xd, xf
     print(json.dumps({"quality": records, "seed": seed, "data": "synthetic"}))
     return 0
+
+
+def graph_us_per_call(torch, call, stream, dev) -> float:
+    """GRAPH_CALLS consecutive calls captured in one HIP graph (as a serving step would be)
+    and replayed; microseconds per call."""
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        call(cap)
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(GRAPH_CALLS):
+                call(cap)
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    settle_clock(torch, graph.replay, stream, min_ms=30.0)
+    ms = timed_calls(torch, graph.replay, stream, 20)
+    del graph
+    return ms * 1e3 / GRAPH_CALLS
+
+
+def other_workloads(torch, np, fc, synth, seed, dev, stream) -> dict:
+    """The other configurations of the path on the same clock: LLaMA-3-8B prefill and the
+    group-size sweep (GB/s, and the sweep's per-stage errors, Figure 4's trend), decode
+    (microseconds per call: one eager launch, inside a HIP graph, and the three stage
+    launches), tiny."""
+    res = {}
+
+    def put(xh, tdt):
+        return torch.from_numpy(xh.view(np.int16)).to(dev).view(tdt)
+
+    # LLaMA-3-8B prefill: the three stage launches, two buffer sets in turn
+    w = synth.workload("llama3_8b_prefill")
+    tdt = torch.float16 if w.dtype == synth.F16 else torch.bfloat16
+    xh = synth.operands(w, seed)
+    xs = [put(xh, tdt) for _ in range(2)]
+    del xh
+    g2 = fc.fc_stage2_group(w.R, w.H, w.group)
+    bufs = [fc.fc_allreduce_emulated(x, w.bits, w.group) for x in xs]
+    it = [0]
+
+    def call8():
+        i = it[0] = it[0] ^ 1
+        fc.fc_allreduce_emulated(xs[i], w.bits, w.group, bufs[i][0], bufs[i][1], stream=stream)
+
+    st = settle_clock(torch, call8, stream)
+    ms = timed_calls(torch, call8, stream, 100)
+    mb = model_bytes(w.R, w.T, w.H, w.bits, w.group, g2)["total"]
+    res["llama3_8b_prefill"] = {
+        "R": w.R, "T": w.T, "H": w.H, "io_dtype": w.dtype, "bits": w.bits, "group": w.group,
+        "ms_per_step": round(ms, 6), "gbps": round(mb / (ms * 1e-3) / 1e9, 1),
+        "pct_of_peak": round(100 * mb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+        "model_bytes": mb, "steps": 100, "settle": st}
+    del xs, bufs
+    torch.cuda.empty_cache()
+
+    # the group-size sweep: one set of operands for every width and group length
+    base = synth.workload("sweep_int4_g128")
+    tdt = torch.float16 if base.dtype == synth.F16 else torch.bfloat16
+    xh = synth.operands(base, seed)
+    xd = put(xh, tdt)
+    del xh
+    xf = xd.float()
+    sweep = []
+    for bits in synth.SWEEP_BITS:
+        for g in synth.SWEEP_GROUPS:
+            R, T, H = base.R, base.T, base.H
+            g2 = fc.fc_stage2_group(R, H, g)
+            out, ws = fc.fc_allreduce_emulated(xd, bits, g)
+            rec = {"bits": bits, "group": g, "group2": g2}
+            rec.update(stage_errors(torch, fc, xf, out, ws, R, T, H, bits, bits, g, g2))
+
+            def calls(bits=bits, g=g, out=out, ws=ws):
+                fc.fc_allreduce_emulated(xd, bits, g, out, ws, stream=stream)
+
+            settle_clock(torch, calls, stream, min_ms=30.0)
+            ms = timed_calls(torch, calls, stream, 50)
+            mb = model_bytes(R, T, H, bits, g, g2)["total"]
+            rec.update({"us_per_step": round(ms * 1e3, 2), "gbps": round(mb / (ms * 1e-3) / 1e9, 1)})
+            sweep.append(rec)
+            del out, ws
+    res["sweep"] = {"R": base.R, "T": base.T, "H": base.H, "io_dtype": base.dtype,
+                    "note": "one input set; the same inputs read by every step (cache-warm)",
+                    "points": sweep}
+    del xd, xf
+    torch.cuda.empty_cache()
+
+    # launch-bound shapes: decode and tiny
+    for name in ("decode", "tiny"):
+        w = synth.workload(name)
+        tdt = torch.float16 if w.dtype == synth.F16 else torch.bfloat16
+        xd = put(synth.operands(w, seed), tdt)
+        g2 = fc.fc_stage2_group(w.R, w.H, w.group)
+        out, ws = fc.fc_allreduce_emulated(xd, w.bits, w.group)
+        v = fc.workspace_views(ws, w.R, w.T, w.H, w.bits, w.group)
+
+        def single(s=stream):
+            fc.fc_allreduce_emulated(xd, w.bits, w.group, out, ws, stream=s)
+
+        def three(s=stream):
+            fc.fc_quantize_groups(xd, w.bits, w.group, v["codes1"], v["s1"], v["z1"], stream=s)
+            fc.fc_dequant_sum_requant(v["codes1"], v["s1"], v["z1"], w.R, w.T, w.H, w.bits, w.group,
+                                      v["codes2"], v["s2"], v["z2"], stream=s)
+            fc.fc_dequantize(v["codes2"], v["s2"], v["z2"], w.T, w.H, w.bits, g2, tdt, out, stream=s)
+
+        settle_clock(torch, single, stream, min_ms=30.0)
+        us_single = timed_calls(torch, single, stream, 200) * 1e3
+        settle_clock(torch, three, stream, min_ms=30.0)
+        us_three = timed_calls(torch, three, stream, 200) * 1e3
+        us_graph = graph_us_per_call(torch, single, stream, dev)
+        mb = model_bytes(w.R, w.T, w.H, w.bits, w.group, g2)["total"]
+        res[name] = {"R": w.R, "T": w.T, "H": w.H, "io_dtype": w.dtype, "bits": w.bits,
+                     "group": w.group, "model_bytes": mb,
+                     "us_per_call_single_launch": round(us_single, 2),
+                     "us_per_call_in_graph": round(us_graph, 2),
+                     "us_per_call_three_launches": round(us_three, 2),
+                     "gbps_single_launch": round(mb / (us_single * 1e-6) / 1e9, 1),
+                     "graph_calls_per_replay": GRAPH_CALLS,
+                     "timing": "HIP events around 200 back-to-back calls through the Python "
+                               "binding (launch cost included), after a settle run"}
+        del xd, out, ws, v
+    return res
+
+
+def stream_ceilings(torch, fc, dev, stream, nbytes: int) -> dict:
+    """GB/s of the library's plain streaming kernels over nbytes of source (the best of 2, 4
+    and 8 loads in flight per lane): copy, read 4 / write 1 (K1's shape), read only."""
+    L = fc.lib()
+    probe = L.fc_internal_stream_probe
+    probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                      ctypes.c_void_p]
+    probe.restype = ctypes.c_int
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.random_(0, 256)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    moved = {0: 2 * nbytes, 1: nbytes + nbytes // 4, 2: nbytes}
+    names = {0: "copy", 1: "read4_write1", 2: "read"}
+    out = {}
+    for kind in (0, 1, 2):
+        best = None
+        for slots in (2, 4, 8):
+            def run(kind=kind, slots=slots):
+                rc = probe(kind, slots, ctypes.c_void_p(src.data_ptr()),
+                           ctypes.c_void_p(dst.data_ptr()), nbytes, sp)
+                if rc != 0:
+                    raise RuntimeError(f"fc_internal_stream_probe returned {rc}")
+            settle_clock(torch, run, stream, min_ms=20.0)
+            ms = timed_calls(torch, run, stream, 20)
+            gbps = moved[kind] / (ms * 1e-3) / 1e9
+            if best is None or gbps > best["gbps"]:
+                best = {"gbps": round(gbps, 1), "slots": slots, "us": round(ms * 1e3, 2)}
+        out[names[kind]] = best
+    out["source_bytes"] = nbytes
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
 
 
 def main() -> int:
@@ -239,6 +445,8 @@ def main() -> int:
                     help="skip the linear-layer leg (the GEMM with the quantizer in its epilogue)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the CPU oracle (profiling runs)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the headline and its per-kernel pass (profiling runs)")
     ap.add_argument("--quality", action="store_true",
                     help="instead of the benchmark: error (MSE) of both stages and throughput for "
                          "every block size and width of the sweep and for the five workloads")
@@ -288,206 +496,64 @@ def main() -> int:
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
-    def step(i: int, k1_ev=None, all_ev=None) -> None:
+    def step(i: int, ev=None) -> None:
         xd, c1, s1, z1, c2, s2, z2, out = sets[i % 2]
-        if k1_ev is not None:
-            k1_ev[0].record(stream)
-        if all_ev is not None:
-            all_ev[0].record(stream)
+        if ev is not None:
+            ev[0].record(stream)
         fc.fc_quantize_groups(xd, bits, group, c1, s1, z1, stream=stream)
-        if k1_ev is not None:
-            k1_ev[1].record(stream)
-        if all_ev is not None:
-            all_ev[1].record(stream)
+        if ev is not None:
+            ev[1].record(stream)
         fc.fc_dequant_sum_requant(c1, s1, z1, R, T, H, bits, group, c2, s2, z2, stream=stream)
-        if all_ev is not None:
-            all_ev[2].record(stream)
+        if ev is not None:
+            ev[2].record(stream)
         fc.fc_dequantize(c2, s2, z2, T, H, bits, g2, tdt, out, stream=stream)
-        if all_ev is not None:
-            all_ev[3].record(stream)
+        if ev is not None:
+            ev[3].record(stream)
 
+    counter = [0]
+
+    def next_step() -> None:
+        step(counter[0])
+        counter[0] += 1
+
+    # 1. settle at the steady clock; 2. W warm-up steps; K timed steps, no events
+    print("[bench] settling", file=sys.stderr, flush=True)
+    settle = settle_clock(torch, next_step, stream)
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-
-    # Timed region: K steps. The only events in it bracket K1, the kernel
-    # whose roofline is reported, on a sample of the steps (every
-    # K1_SAMPLE_EVERY-th, at least 20 of them when K allows): each event is a
-    # packet in the stream that adds a few microseconds between kernels, so
-    # bracketing every launch would slow the whole step down. The K2/K3 split
-    # is timed separately below.
     K = args.steps
-    every = k1_sample_every(K)
-    k1_events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-                 for i in range(0, K, every)}
     print(f"[bench] timing {K} steps after {args.warmup} warmup", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(i, k1_ev=k1_events.get(i))
+        step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
-    k1_ms = np.array([ev[0].elapsed_time(ev[1]) for ev in k1_events.values()])
 
-    # Per-kernel breakdown (not part of the timed region).
-    KB = min(K, 50)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(KB)]
-    for i in range(KB):
-        step(i, all_ev=events[i])
+    # 3. per-kernel pass: events around each kernel of BREAKDOWN_STEPS steps
+    events = [_events(torch, 4) for _ in range(BREAKDOWN_STEPS)]
+    for i in range(BREAKDOWN_STEPS):
+        step(i, ev=events[i])
     torch.cuda.synchronize()
     k_ms = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(3)] for ev in events])
     k_avg = k_ms.mean(axis=0)
     k_med = np.median(k_ms, axis=0)
     pipe_ms = np.array([ev[0].elapsed_time(ev[3]) for ev in events])
 
-    # a plain device-to-device copy of 1 GiB: the runtime's own streaming kernel
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ce[0].record(stream)
-    for _ in range(10):
-        dst.copy_(src)
-    ce[1].record(stream)
+    # 4. cold start: the same K steps after the GPU has been idle
+    time.sleep(COLD_IDLE_S)
     torch.cuda.synchronize()
-    copy_gbps = 2 * (1 << 30) * 10 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
-    del src, dst
-
-    # The uncompressed all-reduce result on the same operands: the arithmetic of
-    # the ring all-reduce the method replaces, as an on-GPU comparator.
-    xd0 = sets[0][0]
-    sum_out = torch.empty((T, H), dtype=tdt, device=dev)
-    for _ in range(5):
-        fc.fc_sum_uncompressed(xd0, sum_out, stream=stream)
-    se = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    se[0].record(stream)
-    for _ in range(50):
-        fc.fc_sum_uncompressed(xd0, sum_out, stream=stream)
-    se[1].record(stream)
+    c0 = time.perf_counter()
+    for i in range(K):
+        step(i)
     torch.cuda.synchronize()
-    sum_ms = se[0].elapsed_time(se[1]) / 50
-    sum_bytes = (R + 1) * T * H * 2
-    # codec output vs the uncompressed result (diagnostic, in torch on the GPU)
-    step(0)
-    torch.cuda.synchronize()
-    diff = sets[0][7].float() - sum_out.float()
-    mse = float((diff * diff).mean())
-    ref_pow = float((sum_out.float() ** 2).mean())
-    del diff
-
-    # The residual add of the transformer block folded into the final step,
-    # against the same result computed unfused (dequantize, then torch's add).
-    xd0, c1, s1, z1, c2, s2, z2, out0 = sets[0]
-    residual = torch.empty((T, H), dtype=tdt, device=dev).normal_(0.0, 2.0)
-    res_out = torch.empty_like(residual)
-    tmp = torch.empty_like(residual)
-
-    def fused_res():
-        fc.fc_dequantize_residual(c2, s2, z2, T, H, bits, g2, residual, res_out, stream=stream)
-
-    def unfused_res():
-        fc.fc_dequantize(c2, s2, z2, T, H, bits, g2, tdt, tmp, stream=stream)
-        torch.add(residual, tmp, out=res_out)
-
-    def timed(fn, n=50):
-        for _ in range(5):
-            fn()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record(stream)
-        for _ in range(n):
-            fn()
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[1]) / n
-
-    pay2 = T * H * bits // 8 + T * (H // g2) * 4
-    res_fused_ms = timed(fused_res)
-    res_unfused_ms = timed(unfused_res)
-    residual_add = {
-        "fused_ms": round(res_fused_ms, 5),
-        "fused_bytes": pay2 + 2 * T * H * 2,
-        "fused_gbps": round((pay2 + 2 * T * H * 2) / (res_fused_ms * 1e-3) / 1e9, 1),
-        "unfused_ms": round(res_unfused_ms, 5),
-        "unfused_bytes": pay2 + 4 * T * H * 2,
-        "speedup": round(res_unfused_ms / res_fused_ms, 3),
-    }
-    del residual, res_out, tmp
-
-    # The row-parallel linear layers in front of the all-reduce (Figure 5,
-    # left: the attention output projection o_proj, K = H / R input features
-    # per rank, and the MLP down projection d_proj, K = ffn / R) with the
-    # stage-1 quantization in the GEMM's epilogue, against the unfused pair
-    # (torch's batched GEMM writing y, then the stage-1 kernel reading it back).
-    linear = None
-    if not args.no_linear:
-        linear = {}
-        shapes = [("o_proj", H // R)] + ([("d_proj", w.ffn // R)] if w.ffn else [])
-        for name, Kl in shapes:
-            if Kl % 32 or H % 256 or group > 256:
-                continue
-            gen = torch.Generator(device=dev).manual_seed(args.seed)
-            la = torch.randn((R, T, Kl), generator=gen, device=dev, dtype=torch.float32).to(tdt)
-            lw = (torch.randn((R, H, Kl), generator=gen, device=dev, dtype=torch.float32)
-                  / Kl ** 0.5).to(tdt)
-            lwt = lw.transpose(1, 2).contiguous()           # [R, K, H] for torch.bmm
-            ly = torch.empty((R, T, H), dtype=tdt, device=dev)
-
-            def fused_lin():
-                fc.fc_linear_quantize(la, lw, bits, group, c1, s1, z1, stream=stream)
-
-            def gemm_only():
-                torch.bmm(la, lwt, out=ly)
-
-            def unfused_lin():
-                torch.bmm(la, lwt, out=ly)
-                fc.fc_quantize_groups(ly, bits, group, c1, s1, z1, stream=stream)
-
-            flops = 2.0 * R * T * H * Kl
-            n_it = max(3, min(20, int(2e13 / flops)))
-            # three rounds, the variants interleaved, median per variant: the
-            # first launches after a change of shape or kernel run slower
-            rounds = [[timed(fn, n_it) for fn in (fused_lin, gemm_only, unfused_lin)]
-                      for _ in range(LINEAR_ROUNDS)]
-            lin_ms, gemm_ms, unf_ms = (sorted(col)[len(col) // 2] for col in zip(*rounds))
-            tf = flops / (lin_ms * 1e-3) / 1e12
-            linear[name] = {
-                "shape": {"R": R, "T": T, "K": Kl, "H": H},
-                "fused_ms": round(lin_ms, 4),
-                "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                             "timing": f"HIP events around {n_it} back-to-back launches, median of "
-                                       f"{LINEAR_ROUNDS} rounds interleaved with the unfused variants"},
-                "torch_gemm_ms": round(gemm_ms, 4),
-                "torch_gemm_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
-                "unfused_ms": round(unf_ms, 4),
-                "speedup_vs_unfused": round(unf_ms / lin_ms, 3),
-            }
-            del la, lw, lwt, ly
-            torch.cuda.empty_cache()
+    cold_ms = (time.perf_counter() - c0) * 1e3 / K
 
     value = mb["total"] / (ms_per_step * 1e-3) / 1e9
-    k1_avg_ms = float(k1_ms.mean())
+    k1_avg_ms = float(k_avg[0])
     k1_gbps = mb["k1"] / (k1_avg_ms * 1e-3) / 1e9
     traffic = measured_traffic(w.name)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        print(f"[bench] timing the CPU oracle on the full workload ({CPU_PASSES} passes, 1 thread)",
-              file=sys.stderr, flush=True)
-        passes = []
-        for _ in range(CPU_PASSES):
-            c0 = time.perf_counter()
-            oracle.allreduce(x_host, w.dtype, bits, group, want_f32=False)
-            passes.append(time.perf_counter() - c0)
-        c_s = sorted(passes)[len(passes) // 2]
-        cpu = {"value": round(mb["total"] / c_s / 1e9, 4), "unit": "GB/s", "cores": 1,
-               "kind": "oracle",
-               "sample": f"the whole {w.name} workload (R={R}, T={T}, H={H}), single thread, "
-                         f"median of {CPU_PASSES} passes: {c_s:.2f} s per pass "
-                         f"({sum(passes):.1f} s in all) on {cpu_model()}"}
 
     rec = {
         "metric": METRIC,
@@ -508,7 +574,14 @@ def main() -> int:
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "elements_per_s": round(R * T * H / (ms_per_step * 1e-3), 1),
         "model_bytes": mb,
-        "breakdown_steps": KB,
+        "settle": dict(settle, note="pipeline steps run back to back before the warm-up steps "
+                                    "until the time per step is steady (the GPU's power "
+                                    "management lowers the engine clock for the first ~15 ms "
+                                    "of load after idle)"),
+        "cold_start": {"idle_s_before": COLD_IDLE_S, "ms_per_step": round(cold_ms, 6),
+                       "gbps": round(mb["total"] / (cold_ms * 1e-3) / 1e9, 1),
+                       "note": "the same K steps started after the GPU was idle (no settle)"},
+        "breakdown_steps": BREAKDOWN_STEPS,
         "kernel_ms_avg": {"k1_quantize": round(float(k_avg[0]), 5),
                           "k2_dequant_sum_requant": round(float(k_avg[1]), 5),
                           "k3_dequantize": round(float(k_avg[2]), 5)},
@@ -526,22 +599,156 @@ def main() -> int:
         "pipeline_ms_p10_p90_events": [round(float(np.percentile(pipe_ms, 10)), 5),
                                        round(float(np.percentile(pipe_ms, 90)), 5)],
         "input_checksum": {"seed": args.seed, "blake2b_64": x_checksum},
-        "copy_ceiling_gbps": round(copy_gbps, 1),
-        "uncompressed_sum": {"ms": round(sum_ms, 5), "bytes": sum_bytes,
-                             "gbps": round(sum_bytes / (sum_ms * 1e-3) / 1e9, 1),
-                             "codec_mse_vs_uncompressed": mse,
-                             "codec_snr_db": round(10 * np.log10(ref_pow / mse), 2) if mse > 0 else None},
         "link_bytes_per_rank": link_bytes(R, T, H, bits, group, g2),
-        "residual_add": residual_add,
-        "linear_quantize": linear,
         "roofline": {"bound": "hbm", "kernel": "k1_quantize", "achieved": round(k1_gbps, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(k1_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": mb["k1"],
                      "avg_launch_ms": round(k1_avg_ms, 5),
-                     "timing": f"HIP events around the K1 launch of one timed step in {every} "
-                               f"({len(k1_ms)} launches)"},
-        "cpu_baseline": cpu,
+                     "timing": f"HIP events on the launch stream around K1 in each of "
+                               f"{BREAKDOWN_STEPS} pipeline steps run right after the timed region "
+                               f"(the bracket includes the dispatch gap before the kernel)",
+                     "traffic_note": "FETCH_SIZE + WRITE_SIZE (rocprofv3) per launch, calibrated "
+                                     "on a copy of known size: bytes between L2 and the data "
+                                     "fabric, which count Infinity Cache hits as well as DRAM"},
     }
+
+    if not args.no_extras:
+        print("[bench] streaming ceilings", file=sys.stderr, flush=True)
+        ceil = stream_ceilings(torch, fc, dev, stream, R * T * H * 2)
+        ceil["k1_frac_of_read4_write1"] = round(k1_gbps / ceil["read4_write1"]["gbps"], 4)
+        rec["stream_ceilings_gbps"] = ceil
+
+        # The uncompressed all-reduce result on the same operands: the arithmetic of
+        # the ring all-reduce the method replaces, as an on-GPU comparator.
+        xd0 = sets[0][0]
+        sum_out = torch.empty((T, H), dtype=tdt, device=dev)
+
+        def sum_call():
+            fc.fc_sum_uncompressed(xd0, sum_out, stream=stream)
+
+        settle_clock(torch, sum_call, stream, min_ms=30.0)
+        sum_ms = timed_calls(torch, sum_call, stream, 50)
+        sum_bytes = (R + 1) * T * H * 2
+        step(0)
+        torch.cuda.synchronize()
+        diff = sets[0][7].float() - sum_out.float()
+        mse = float((diff * diff).mean())
+        ref_pow = float((sum_out.float() ** 2).mean())
+        del diff
+        rec["uncompressed_sum"] = {
+            "ms": round(sum_ms, 5), "bytes": sum_bytes,
+            "gbps": round(sum_bytes / (sum_ms * 1e-3) / 1e9, 1),
+            "codec_mse_vs_uncompressed": mse,
+            "codec_snr_db": round(10 * np.log10(ref_pow / mse), 2) if mse > 0 else None}
+
+        # The residual add of the transformer block folded into the final step,
+        # against the same result computed unfused (dequantize, then torch's add).
+        xd0, c1, s1, z1, c2, s2, z2, out0 = sets[0]
+        residual = torch.empty((T, H), dtype=tdt, device=dev).normal_(0.0, 2.0)
+        res_out = torch.empty_like(residual)
+        tmp = torch.empty_like(residual)
+
+        def fused_res():
+            fc.fc_dequantize_residual(c2, s2, z2, T, H, bits, g2, residual, res_out, stream=stream)
+
+        def unfused_res():
+            fc.fc_dequantize(c2, s2, z2, T, H, bits, g2, tdt, tmp, stream=stream)
+            torch.add(residual, tmp, out=res_out)
+
+        pay2 = mb["payload2"]
+        settle_clock(torch, fused_res, stream, min_ms=30.0)
+        res_fused_ms = timed_calls(torch, fused_res, stream, 50)
+        settle_clock(torch, unfused_res, stream, min_ms=30.0)
+        res_unfused_ms = timed_calls(torch, unfused_res, stream, 50)
+        rec["residual_add"] = {
+            "fused_ms": round(res_fused_ms, 5),
+            "fused_bytes": pay2 + 2 * T * H * 2,
+            "fused_gbps": round((pay2 + 2 * T * H * 2) / (res_fused_ms * 1e-3) / 1e9, 1),
+            "unfused_ms": round(res_unfused_ms, 5),
+            "unfused_bytes": pay2 + 4 * T * H * 2,
+            "speedup": round(res_unfused_ms / res_fused_ms, 3),
+        }
+        del residual, res_out, tmp, sum_out
+
+        # The row-parallel linear layers in front of the all-reduce (Figure 5,
+        # left: the attention output projection o_proj, K = H / R input features
+        # per rank, and the MLP down projection d_proj, K = ffn / R) with the
+        # stage-1 quantization in the GEMM's epilogue, against the unfused pair
+        # (torch's batched GEMM writing y, then the stage-1 kernel reading it back).
+        linear = None
+        if not args.no_linear:
+            linear = {}
+            shapes = [("o_proj", H // R)] + ([("d_proj", w.ffn // R)] if w.ffn else [])
+            for name, Kl in shapes:
+                if Kl % 32 or H % 256 or group > 256:
+                    continue
+                gen = torch.Generator(device=dev).manual_seed(args.seed)
+                la = torch.randn((R, T, Kl), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+                lw = (torch.randn((R, H, Kl), generator=gen, device=dev, dtype=torch.float32)
+                      / Kl ** 0.5).to(tdt)
+                lwt = lw.transpose(1, 2).contiguous()           # [R, K, H] for torch.bmm
+                ly = torch.empty((R, T, H), dtype=tdt, device=dev)
+
+                def fused_lin():
+                    fc.fc_linear_quantize(la, lw, bits, group, c1, s1, z1, stream=stream)
+
+                def gemm_only():
+                    torch.bmm(la, lwt, out=ly)
+
+                def unfused_lin():
+                    torch.bmm(la, lwt, out=ly)
+                    fc.fc_quantize_groups(ly, bits, group, c1, s1, z1, stream=stream)
+
+                flops = 2.0 * R * T * H * Kl
+                n_it = max(3, min(20, int(2e13 / flops)))
+                settle_clock(torch, fused_lin, stream, min_ms=30.0)
+                # three rounds, the variants interleaved, median per variant: the
+                # first launches after a change of shape or kernel run slower
+                rounds = [[timed_calls(torch, fn, stream, n_it)
+                           for fn in (fused_lin, gemm_only, unfused_lin)]
+                          for _ in range(LINEAR_ROUNDS)]
+                lin_ms, gemm_ms, unf_ms = (sorted(col)[len(col) // 2] for col in zip(*rounds))
+                tf = flops / (lin_ms * 1e-3) / 1e12
+                linear[name] = {
+                    "shape": {"R": R, "T": T, "K": Kl, "H": H},
+                    "fused_ms": round(lin_ms, 4),
+                    "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                                 "timing": f"HIP events around {n_it} back-to-back launches, median "
+                                           f"of {LINEAR_ROUNDS} rounds interleaved with the "
+                                           f"unfused variants"},
+                    "torch_gemm_ms": round(gemm_ms, 4),
+                    "torch_gemm_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
+                    "unfused_ms": round(unf_ms, 4),
+                    "speedup_vs_unfused": round(unf_ms / lin_ms, 3),
+                    "fusion_wins": bool(unf_ms > lin_ms),
+                }
+                del la, lw, lwt, ly
+                torch.cuda.empty_cache()
+        rec["linear_quantize"] = linear
+
+        print("[bench] other workloads", file=sys.stderr, flush=True)
+        rec["other_workloads"] = other_workloads(torch, np, fc, synth, args.seed, dev, stream)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        print(f"[bench] timing the CPU oracle on the full workload ({CPU_PASSES} passes, 1 thread)",
+              file=sys.stderr, flush=True)
+        passes = []
+        for _ in range(CPU_PASSES):
+            c0 = time.perf_counter()
+            oracle.allreduce(x_host, w.dtype, bits, group, want_f32=False)
+            passes.append(time.perf_counter() - c0)
+        c_s = sorted(passes)[len(passes) // 2]
+        hi = host_info()
+        cpu = {"value": round(mb["total"] / c_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"the whole {w.name} workload (R={R}, T={T}, H={H}), single thread, "
+                         f"median of {CPU_PASSES} passes: {c_s:.2f} s per pass "
+                         f"({sum(passes):.1f} s in all) on {hi.get('model name', 'unknown')}",
+               "host": hi}
+    rec["cpu_baseline"] = cpu
     print(json.dumps(rec))
     return 0
 

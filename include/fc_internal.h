@@ -1,0 +1,37 @@
+/*
+ * fc_internal.h -- a measurement helper of libfc.so, not part of the codec's
+ * interface (include/fc.h). The benchmark uses it to measure the bandwidth
+ * ceiling that plain streaming kernels reach on this GPU for the traffic
+ * shapes of the codec's kernels.
+ */
+#ifndef FC_INTERNAL_H_
+#define FC_INTERNAL_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * One streaming pass over `bytes` bytes of `src` (device pointers, 16-byte
+ * aligned, bytes % 16 == 0), enqueued on `stream` (a hipStream_t; NULL = the
+ * default stream):
+ *   kind 0  copy:             dst[0 .. bytes) = src[0 .. bytes)
+ *   kind 1  read 4, write 1:  reads src, writes bytes/4 bytes of dst (one
+ *           4-byte word per 16 bytes read: the xor of its four words)
+ *   kind 2  read:             reads src, writes one 4-byte word per wave
+ *           tile (dst must hold 4 * ceil(bytes / (slots * 1024)) bytes)
+ * slots: 16-byte loads each lane keeps in flight (2, 4 or 8).
+ * Returns 0, or 1 (NULL pointer), 2 (bad kind or slots), 4 (alignment or
+ * size not a multiple of 16), 6 (launch error). bytes == 0 enqueues nothing.
+ * The caller owns both buffers; nothing is allocated.
+ */
+int fc_internal_stream_probe(int kind, int slots, const void *src, void *dst, size_t bytes,
+                             void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FC_INTERNAL_H_ */

@@ -13,13 +13,15 @@ import bit_activation_compression_amd as fc
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fc.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced on the error paths
 MISALIGNED = ctypes.c_void_p(0x10008)
 
 
-def _declared_functions():
-    src = open(HEADER).read()
+def _declared_functions(headers=(HEADER,)):
+    src = "".join(open(h).read() for h in headers)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(fc_[a-z0-9_]+)\s*\(", src)))
 
@@ -31,6 +33,10 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(L, n), n
     assert sorted(names) == sorted(fc.EXPORTED_SYMBOLS)
+    internal = sorted(set(_declared_functions(HEADERS)) - set(names))
+    assert internal == ["fc_internal_stream_probe"]
+    for n in internal:
+        assert hasattr(L, n), n
 
 
 def test_no_kernel_launch_stub_left_undefined():
@@ -186,3 +192,16 @@ def test_noalloc_scratch_size_matches_header():
     src = open(HEADER).read()
     m = re.search(r"#define FC_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
     assert m and int(m.group(1)) << int(m.group(2)) == fc.NOALLOC_SCRATCH_BYTES
+
+
+def test_stream_probe_validates():
+    L = fc.lib()
+    P = L.fc_internal_stream_probe
+    P.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                  ctypes.c_void_p]
+    assert P(3, 4, FAKE, FAKE, 1024, None) == 2
+    assert P(0, 3, FAKE, FAKE, 1024, None) == 2
+    assert P(0, 4, None, FAKE, 1024, None) == 1
+    assert P(0, 4, MISALIGNED, FAKE, 1024, None) == 4
+    assert P(0, 4, FAKE, FAKE, 1000, None) == 4
+    assert P(0, 4, None, None, 0, None) == 0

@@ -54,17 +54,60 @@ def test_more_than_one_gpu_refused():
     assert msg["n_gpus"] == 2 and "single GPU" in msg["error"]
 
 
-def test_k1_event_sampling_stride():
-    """K1 is bracketed by events on every 10th timed step, keeping at least 20
-    samples when the run allows it, and every step of a short run."""
-    assert bench.k1_sample_every(200) == 10
-    assert bench.k1_sample_every(1000) == 10
-    assert bench.k1_sample_every(100) == 5
-    assert bench.k1_sample_every(20) == 1
-    assert bench.k1_sample_every(5) == 1
-    for k in (1, 7, 40, 199, 200, 5000):
-        every = bench.k1_sample_every(k)
-        assert len(range(0, k, every)) >= min(k, 20)
+class _FakeEvent:
+    """Stands in for torch.cuda.Event: elapsed_time() replays scripted block times."""
+    script = []
+
+    def __init__(self, enable_timing=True):
+        self.t = None
+
+    def record(self, stream=None):
+        pass
+
+    def elapsed_time(self, other):
+        return _FakeEvent.script.pop(0)
+
+
+class _FakeTorch:
+    class cuda:
+        Event = _FakeEvent
+
+        @staticmethod
+        def synchronize():
+            pass
+
+
+def test_settle_waits_for_min_time_and_two_agreeing_blocks():
+    # probe: 3 calls in 3 ms -> 1 ms per call -> blocks of SETTLE_BLOCK_MS calls
+    blk = bench.SETTLE_BLOCK_MS
+    n = int(round(blk))
+    per_call = [1.30, 1.25, 1.10, 1.02, 1.001, 1.0, 1.0, 1.0] + [1.0] * 200
+    _FakeEvent.script = [3.0] + [p * n for p in per_call]
+    calls = []
+    st = bench.settle_clock(_FakeTorch, lambda: calls.append(1), None, min_ms=30.0, max_ms=500.0)
+    assert st["steady"]
+    # stops at the first block with >= 30 ms behind it whose time is within 1% of the last
+    elapsed, k = 0.0, 0
+    while True:
+        elapsed += per_call[k] * n
+        if elapsed >= 30.0 and k >= 1 and abs(per_call[k] - per_call[k - 1]) <= 0.01 * per_call[k - 1]:
+            break
+        k += 1
+    assert st["ms"] == round(elapsed, 2)
+    assert st["calls"] == 6 + (k + 1) * n == len(calls)
+    assert st["first_block_ms_per_call"] == round(per_call[0], 5)
+
+
+def test_settle_gives_up_at_max_time():
+    _FakeEvent.script = [3.0] + [float(i % 2 + 1) * 6 for i in range(1000)]
+    st = bench.settle_clock(_FakeTorch, lambda: None, None, min_ms=10.0, max_ms=100.0)
+    assert not st["steady"] and st["ms"] >= 100.0
+
+
+def test_host_info_names_the_processor_count():
+    hi = bench.host_info()
+    assert hi["host_nproc"] == os.cpu_count()
+    assert "platform" in hi
 
 
 def test_k1_hash_ignores_comments_but_not_code():
