@@ -400,8 +400,8 @@ def other_workloads(torch, np, fc, synth, seed, dev, stream) -> dict:
 
 
 def stream_ceilings(torch, fc, dev, stream, nbytes: int) -> dict:
-    """GB/s of the library's plain streaming kernels over nbytes of source (the best of 2, 4
-    and 8 loads in flight per lane): copy, read 4 / write 1 (K1's shape), read only."""
+    """GB/s of the library's plain streaming kernels over nbytes of source (the best of 1, 2,
+    4 and 8 loads in flight per lane): copy, read 4 / write 1 (K1's shape), read only."""
     L = fc.lib()
     probe = L.fc_internal_stream_probe
     probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
@@ -416,7 +416,7 @@ def stream_ceilings(torch, fc, dev, stream, nbytes: int) -> dict:
     out = {}
     for kind in (0, 1, 2):
         best = None
-        for slots in (2, 4, 8):
+        for slots in (1, 2, 4, 8):
             def run(kind=kind, slots=slots):
                 rc = probe(kind, slots, ctypes.c_void_p(src.data_ptr()),
                            ctypes.c_void_p(dst.data_ptr()), nbytes, sp)
@@ -446,7 +446,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the CPU oracle (profiling runs)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="only the headline and its per-kernel pass (profiling runs)")
+                    help="only the headline, its per-kernel pass and the streaming ceilings "
+                         "(profiling runs; the ceilings' copy kernel calibrates the counters)")
     ap.add_argument("--quality", action="store_true",
                     help="instead of the benchmark: error (MSE) of both stages and throughput for "
                          "every block size and width of the sweep and for the five workloads")
@@ -612,11 +613,12 @@ def main() -> int:
                                      "fabric, which count Infinity Cache hits as well as DRAM"},
     }
 
+    print("[bench] streaming ceilings", file=sys.stderr, flush=True)
+    ceil = stream_ceilings(torch, fc, dev, stream, R * T * H * 2)
+    ceil["k1_frac_of_read4_write1"] = round(k1_gbps / ceil["read4_write1"]["gbps"], 4)
+    rec["stream_ceilings_gbps"] = ceil
+
     if not args.no_extras:
-        print("[bench] streaming ceilings", file=sys.stderr, flush=True)
-        ceil = stream_ceilings(torch, fc, dev, stream, R * T * H * 2)
-        ceil["k1_frac_of_read4_write1"] = round(k1_gbps / ceil["read4_write1"]["gbps"], 4)
-        rec["stream_ceilings_gbps"] = ceil
 
         # The uncompressed all-reduce result on the same operands: the arithmetic of
         # the ring all-reduce the method replaces, as an on-GPU comparator.

@@ -362,6 +362,13 @@ __device__ __forceinline__ void dequant8(const uint32_t (&w)[BITS == 4 ? 1 : 2],
 // written to cb (NT: non-temporal) and the fp16 scale and zero of every group
 // to sb and zb (bases of the tile's first group). Slots at or past `avail`
 // elements are not stored.
+//
+// With two slots per tile and groups of one slot spanning at least two
+// lanes, every lane holds values of two groups, and the lanes of a group come
+// in (even, odd) pairs: the even lane computes the scale, zero and reciprocal
+// of its slot-0 group, the odd lane those of its slot-1 group, and each lane
+// takes the other one from its partner (DPP quad_perm [0,0,2,2] and
+// [1,1,3,3]), instead of computing both. The results are the same values.
 template <int BITS, int G, int U, bool NT>
 __device__ __forceinline__ void quantize_tile(const float (&v)[U][kLaneElems], const float (&mn)[U],
                                               const float (&mx)[U], int lane, uint32_t avail,
@@ -370,6 +377,29 @@ __device__ __forceinline__ void quantize_tile(const float (&v)[U][kLaneElems], c
     constexpr int L = G >= kSlotElems ? kWave : G / kLaneElems;   // lanes per group in a slot
     constexpr int W = BITS == 4 ? 1 : 2;
     static_assert(U % S == 0 && (U * kSlotElems) % G == 0, "a tile holds whole groups");
+    if constexpr (U == 2 && S == 1 && L >= 2) {
+        float a0 = mn[0], b0 = mx[0], a1 = mn[1], b1 = mx[1];
+        lanes_minmax<L>(a0, b0);
+        lanes_minmax<L>(a1, b1);
+        const bool odd = (lane & 1) != 0;
+        const GroupParams own = group_params<BITS>(odd ? a1 : a0, odd ? b1 : b0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            GroupParams p = own;
+            p.z = u == 0 ? dpp<0xA0>(own.z) : dpp<0xF5>(own.z);
+            p.inv = u == 0 ? dpp<0xA0>(own.inv) : dpp<0xF5>(own.inv);
+            const uint32_t rel = u * kSlotElems + lane * kLaneElems;
+            if (rel >= avail) continue;
+            uint32_t w[W];
+            encode8<BITS>(v[u], p, w);
+            store_codes<BITS, NT>(cb, rel, w);
+            if (lane % L == u) {   // lane & 1 == u: `own` is this slot's group
+                sb[rel / G] = own.s16;
+                zb[rel / G] = own.z16;
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int g = 0; g < U / S; ++g) {
         float a = mn[g * S], b = mx[g * S];

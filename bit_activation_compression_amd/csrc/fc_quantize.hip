@@ -15,10 +15,14 @@
 namespace fc {
 namespace {
 
-// Tiles of 4 slots (4 KiB of input per wave) with non-temporal loads and
-// code stores measured fastest on MI355X for this read-4 / write-1 stream,
-// counting the effect on the kernel that reads the codes next.
-constexpr int kTileSlots = 4;
+// Tiles of 2 slots (2 KiB of input per wave, two 16-byte loads per lane in
+// flight) with non-temporal loads and code stores. Measured on MI355X inside
+// the whole pipeline: a plain read-4 / write-1 stream of this shape runs at
+// 103 us over the 70B operands against 108 us with 4 slots and 114 us with
+// one, and the quantizer follows it (2 slots 105.6 us, 4 slots 108 us); the
+// pipeline step, which also depends on how K2 then reads the codes, goes
+// from 171.6 to 166.6 us.
+constexpr int kTileSlots = 2;
 
 template <int DT, int BITS, int G>
 __global__ __launch_bounds__(kBlockThreads) void quantize_kernel(

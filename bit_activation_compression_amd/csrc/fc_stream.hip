@@ -74,6 +74,7 @@ hipError_t launch(const void *src, void *dst, uint64_t n, hipStream_t stream) {
 template <int KIND>
 hipError_t launch_u(int slots, const void *src, void *dst, uint64_t n, hipStream_t stream) {
     switch (slots) {
+    case 1: return launch<KIND, 1>(src, dst, n, stream);
     case 2: return launch<KIND, 2>(src, dst, n, stream);
     case 4: return launch<KIND, 4>(src, dst, n, stream);
     case 8: return launch<KIND, 8>(src, dst, n, stream);
@@ -86,7 +87,7 @@ hipError_t launch_u(int slots, const void *src, void *dst, uint64_t n, hipStream
 
 extern "C" int fc_internal_stream_probe(int kind, int slots, const void *src, void *dst,
                                         size_t bytes, void *stream) {
-    if (kind < 0 || kind > 2 || (slots != 2 && slots != 4 && slots != 8)) return 2;
+    if (kind < 0 || kind > 2 || (slots != 1 && slots != 2 && slots != 4 && slots != 8)) return 2;
     if (bytes == 0) return 0;
     if (src == nullptr || dst == nullptr) return 1;
     if (bytes % 16 != 0 || ((uintptr_t)src & 15u) || ((uintptr_t)dst & 15u)) return 4;

@@ -22,7 +22,7 @@ extern "C" {
  *           4-byte word per 16 bytes read: the xor of its four words)
  *   kind 2  read:             reads src, writes one 4-byte word per wave
  *           tile (dst must hold 4 * ceil(bytes / (slots * 1024)) bytes)
- * slots: 16-byte loads each lane keeps in flight (2, 4 or 8).
+ * slots: 16-byte loads each lane keeps in flight (1, 2, 4 or 8).
  * Returns 0, or 1 (NULL pointer), 2 (bad kind or slots), 4 (alignment or
  * size not a multiple of 16), 6 (launch error). bytes == 0 enqueues nothing.
  * The caller owns both buffers; nothing is allocated.

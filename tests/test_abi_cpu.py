@@ -201,6 +201,7 @@ def test_stream_probe_validates():
                   ctypes.c_void_p]
     assert P(3, 4, FAKE, FAKE, 1024, None) == 2
     assert P(0, 3, FAKE, FAKE, 1024, None) == 2
+    assert P(0, 16, FAKE, FAKE, 1024, None) == 2
     assert P(0, 4, None, FAKE, 1024, None) == 1
     assert P(0, 4, MISALIGNED, FAKE, 1024, None) == 4
     assert P(0, 4, FAKE, FAKE, 1000, None) == 4
