@@ -265,6 +265,8 @@ def fc_linear_quantize(a: torch.Tensor, w: torch.Tensor, bits: int, group: int, 
         z1 = torch.empty_like(s1)
     if y is True:
         y = torch.empty((R, T, H), dtype=a.dtype, device=dev)
+    if y is not None and y.dtype != a.dtype:
+        raise ValueError(f"y must have a's dtype ({a.dtype}), not {y.dtype}")
     _room(codes1, "codes1", R * T * H * bits // 8, dev)
     _room(s1, "s1", R * T * (H // group) * 2, dev)
     _room(z1, "z1", R * T * (H // group) * 2, dev)

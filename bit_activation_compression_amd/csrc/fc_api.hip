@@ -8,84 +8,13 @@
 
 #include "fc.h"
 #include "fc_launch.h"
+#include "fc_validate.h"
 
 namespace {
 
-constexpr size_t kSliceAlign = 256;
-constexpr int kMinGroup = 8;
-constexpr int kMaxGroup = 8192;
-// fc_linear_quantize: channel tile, k stage and the largest group (one
-// channel tile row)
-constexpr int kLinearTileN = 256;
-constexpr int kLinearTileK = 32;
-constexpr int kLinearMaxGroup = 256;
-// and the largest K and H whose tile offsets fit the kernel's 32-bit buffer
-// and lane offsets (256 rows of 2K bytes; 256 token rows of H codes)
-constexpr int kLinearMaxK = 1 << 22;
-constexpr int kLinearMaxH = 1 << 24;
-
-bool pow2_in_range(int g) { return g >= kMinGroup && g <= kMaxGroup && (g & (g - 1)) == 0; }
-
-bool aligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-size_t round_up(size_t v) { return (v + kSliceAlign - 1) / kSliceAlign * kSliceAlign; }
-
-// Checks R, T, H, bits and group; on success sets g2 = min(group, H/R).
-fc_status check_shape(int R, int T, int H, int bits, int group, int *g2) {
-    if (bits != 4 && bits != 8) return FC_ERR_BITS;
-    if (R < 1 || T < 0 || H < 1) return FC_ERR_SHAPE;
-    if (!pow2_in_range(group) || H % group != 0) return FC_ERR_SHAPE;
-    if (H % R != 0) return FC_ERR_SHAPE;
-    const int C = H / R;
-    const int g = group < C ? group : C;
-    if (!pow2_in_range(g) || C % g != 0) return FC_ERR_SHAPE;
-    *g2 = g;
-    return FC_OK;
-}
-
-fc_status check_ptrs(size_t n, std::initializer_list<const void *> ptrs) {
-    if (n == 0) return FC_OK;
-    for (const void *p : ptrs)
-        if (p == nullptr) return FC_ERR_NULL;
-    for (const void *p : ptrs)
-        if (!aligned(p)) return FC_ERR_ALIGN;
-    return FC_OK;
-}
+using namespace fc::validate;
 
 fc_status from_hip(hipError_t e) { return e == hipSuccess ? FC_OK : FC_ERR_LAUNCH; }
-
-struct Layout {
-    size_t off[6];
-    size_t size[6];
-    size_t total;
-};
-
-Layout layout(int R, int T, int H, int bits1, int bits2, int group, int g2) {
-    const size_t n1 = (size_t)R * (size_t)T * (size_t)H;
-    const size_t n2 = (size_t)T * (size_t)H;
-    Layout L;
-    L.size[0] = n1 * (size_t)bits1 / 8;
-    L.size[1] = n1 / (size_t)group * 2;
-    L.size[2] = L.size[1];
-    L.size[3] = n2 * (size_t)bits2 / 8;
-    L.size[4] = n2 / (size_t)g2 * 2;
-    L.size[5] = L.size[4];
-    size_t o = 0;
-    for (int i = 0; i < 6; ++i) {
-        L.off[i] = o;
-        o += round_up(L.size[i]);
-    }
-    L.total = o;
-    return L;
-}
-
-// Shape and both code widths; on success sets g2.
-fc_status check_shape2(int R, int T, int H, int bits1, int bits2, int group, int *g2) {
-    fc_status st = check_shape(R, T, H, bits1, group, g2);
-    if (st != FC_OK) return st;
-    if (bits2 != 4 && bits2 != 8) return FC_ERR_BITS;
-    return FC_OK;
-}
 
 // The emulated all-reduce: the three stage launches, or for launch-bound
 // shapes (decode-sized) the single launch that computes the same payloads and

@@ -108,9 +108,11 @@ fc_status fc_dequantize(const uint8_t *codes2, const uint16_t *s2, const uint16_
                         int T, int H, int bits, int group2, fc_dtype dt, void *out, void *stream);
 
 /*
- * The whole emulated all-reduce on one GPU: fc_quantize_groups, then
- * fc_dequant_sum_requant, then fc_dequantize, with both payloads placed in the
- * caller's workspace (layout: fc_workspace_layout). out [T][H] in dt.
+ * The whole emulated all-reduce on one GPU (TL;DR: the "two-step All-Reduce"
+ * that replaces a ring; Figure 5, right: quantize, Reduce-Scatter, quantize,
+ * All-Gather, dequantize): fc_quantize_groups, then fc_dequant_sum_requant,
+ * then fc_dequantize, with both payloads placed in the caller's workspace
+ * (layout: fc_workspace_layout). out [T][H] in dt.
  * Launch-bound calls (R*T*H <= 2^24, R <= 8, group == stage-2 group <= 512)
  * run as one kernel launch that writes the same payloads and output, bit for
  * bit; larger ones as the three launches.

@@ -63,6 +63,13 @@ def test_layout_dtype_and_device_are_checked():
                                                              device="cuda"))
     with pytest.raises(ValueError, match="GPU tensor"):
         fc.fc_sum_uncompressed(x, out=torch.empty((8, 256), dtype=x.dtype))
+    # the layer output must have the operands' dtype (a float32 buffer of the same
+    # byte count would otherwise receive 16-bit values)
+    a = _x(2, 8, 64)
+    w = _x(2, 256, 64)
+    with pytest.raises(ValueError, match="y must have a's dtype"):
+        fc.fc_linear_quantize(a, w, 4, 128, y=torch.empty((2, 8, 128), dtype=torch.float32,
+                                                          device="cuda"))
 
 
 def test_library_status_becomes_fc_error():
