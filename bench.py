@@ -362,6 +362,27 @@ def other_workloads(torch, np, fc, synth, seed, dev, stream) -> dict:
     del xd, xf
     torch.cuda.empty_cache()
 
+    # the generic kernels: a hidden size of 5120 (not a power of two; LLaMA-2-13B's) and
+    # groups of 160, which the power-of-two kernels do not take
+    w = synth.workload("llama3_8b_prefill").with_(T=4096, H=5120, group=160, name="generic_h5120_g160")
+    tdt = torch.float16 if w.dtype == synth.F16 else torch.bfloat16
+    xd = put(synth.operands(w, seed), tdt)
+    out, ws = fc.fc_allreduce_emulated(xd, w.bits, w.group)
+    g2 = fc.fc_stage2_group(w.R, w.H, w.group)
+
+    def callg():
+        fc.fc_allreduce_emulated(xd, w.bits, w.group, out, ws, stream=stream)
+
+    settle_clock(torch, callg, stream, min_ms=30.0)
+    ms = timed_calls(torch, callg, stream, 20)
+    mb = model_bytes(w.R, w.T, w.H, w.bits, w.group, g2)["total"]
+    res["generic_group"] = {"R": w.R, "T": w.T, "H": w.H, "io_dtype": w.dtype, "bits": w.bits,
+                            "group": w.group, "group2": g2, "us_per_step": round(ms * 1e3, 2),
+                            "gbps": round(mb / (ms * 1e-3) / 1e9, 1),
+                            "note": "generic kernels (group not a power of two); same inputs "
+                                    "every step"}
+    del xd, out, ws
+
     # launch-bound shapes: decode and tiny
     for name in ("decode", "tiny"):
         w = synth.workload(name)

@@ -245,7 +245,7 @@ hipError_t by_bits(const uint16_t *x, int R, uint64_t n, int bits1, int bits2, i
 
 bool allreduce_small_applies(int R, uint64_t n, int group, int group2) {
     return R >= 1 && R <= kMaxR && group == group2 && group >= kLaneElems && group <= kSlotElems &&
-           (uint64_t)R * n <= kAllreduceSmallMaxElems;
+           (group & (group - 1)) == 0 && (uint64_t)R * n <= kAllreduceSmallMaxElems;
 }
 
 hipError_t launch_allreduce_small(const uint16_t *x, int dtype, int R, uint64_t n, int bits1,

@@ -16,6 +16,37 @@ using namespace fc::validate;
 
 fc_status from_hip(hipError_t e) { return e == hipSuccess ? FC_OK : FC_ERR_LAUNCH; }
 
+// The three steps on the fast kernels for power-of-two groups in [8, 8192],
+// on the generic ones otherwise.
+hipError_t run_quantize(const void *x, fc_dtype dt, uint64_t n, int bits, int group, uint8_t *codes,
+                        uint16_t *s, uint16_t *z, hipStream_t stream) {
+    const uint16_t *xv = static_cast<const uint16_t *>(x);
+    return pow2_in_range(group) ? fc::launch_quantize(xv, (int)dt, n, bits, group, codes, s, z, stream)
+                                : fc::launch_quantize_generic(xv, (int)dt, n, bits, group, codes, s, z,
+                                                              stream);
+}
+
+hipError_t run_dsr(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1, int R, uint64_t n,
+                   int bits1, int bits2, int group, int g2, uint8_t *codes2, uint16_t *s2,
+                   uint16_t *z2, hipStream_t stream) {
+    if (pow2_in_range(group) && pow2_in_range(g2))
+        return fc::launch_dequant_sum_requant(codes1, s1, z1, R, n, bits1, bits2, group, g2, codes2,
+                                              s2, z2, stream);
+    return fc::launch_dsr_generic(codes1, s1, z1, R, n, bits1, bits2, group, g2, codes2, s2, z2,
+                                  stream);
+}
+
+hipError_t run_dequantize(const uint8_t *codes2, const uint16_t *s2, const uint16_t *z2, uint64_t n,
+                          int bits, int g2, fc_dtype dt, const void *residual, void *out,
+                          hipStream_t stream) {
+    const uint16_t *rv = static_cast<const uint16_t *>(residual);
+    uint16_t *ov = static_cast<uint16_t *>(out);
+    if (!pow2_in_range(g2))
+        return fc::launch_dequantize_generic(codes2, s2, z2, n, bits, g2, (int)dt, rv, ov, stream);
+    return rv ? fc::launch_dequantize_residual(codes2, s2, z2, n, bits, g2, (int)dt, rv, ov, stream)
+              : fc::launch_dequantize(codes2, s2, z2, n, bits, g2, (int)dt, ov, stream);
+}
+
 // The emulated all-reduce: the three stage launches, or for launch-bound
 // shapes (decode-sized) the single launch that computes the same payloads and
 // output; with_residual: the result is added to `residual`.
@@ -46,18 +77,12 @@ fc_status allreduce_emulated(const void *x, fc_dtype dt, int R, int T, int H, in
             static_cast<const uint16_t *>(x), (int)dt, R, n, bits1, bits2, group, codes1, s1, z1,
             codes2, s2, z2, with_residual ? static_cast<const uint16_t *>(residual) : nullptr,
             static_cast<uint16_t *>(out), s));
-    st = from_hip(fc::launch_quantize(static_cast<const uint16_t *>(x), (int)dt, n * (uint64_t)R, bits1,
-                                      group, codes1, s1, z1, s));
+    st = from_hip(run_quantize(x, dt, n * (uint64_t)R, bits1, group, codes1, s1, z1, s));
     if (st != FC_OK) return st;
-    st = from_hip(fc::launch_dequant_sum_requant(codes1, s1, z1, R, n, bits1, bits2, group, g2, codes2,
-                                                 s2, z2, s));
+    st = from_hip(run_dsr(codes1, s1, z1, R, n, bits1, bits2, group, g2, codes2, s2, z2, s));
     if (st != FC_OK) return st;
-    if (with_residual)
-        return from_hip(fc::launch_dequantize_residual(codes2, s2, z2, n, bits2, g2, (int)dt,
-                                                       static_cast<const uint16_t *>(residual),
-                                                       static_cast<uint16_t *>(out), s));
-    return from_hip(fc::launch_dequantize(codes2, s2, z2, n, bits2, g2, (int)dt,
-                                          static_cast<uint16_t *>(out), s));
+    return from_hip(run_dequantize(codes2, s2, z2, n, bits2, g2, dt,
+                                   with_residual ? residual : nullptr, out, s));
 }
 
 // Payload scratch of fc_allreduce_emulated_noalloc: one array per device
@@ -98,8 +123,8 @@ fc_status fc_quantize_groups(const void *x, fc_dtype dt, int R, int T, int H, in
     const uint64_t n = (uint64_t)R * (uint64_t)T * (uint64_t)H;
     st = check_ptrs(n, {x, codes1, s1, z1});
     if (st != FC_OK || n == 0) return st;
-    return from_hip(fc::launch_quantize(static_cast<const uint16_t *>(x), (int)dt, n, bits, group,
-                                        codes1, s1, z1, static_cast<hipStream_t>(stream)));
+    return from_hip(run_quantize(x, dt, n, bits, group, codes1, s1, z1,
+                                 static_cast<hipStream_t>(stream)));
 }
 
 fc_status fc_dequant_sum_requant_mixed(const uint8_t *codes1, const uint16_t *s1,
@@ -112,8 +137,8 @@ fc_status fc_dequant_sum_requant_mixed(const uint8_t *codes1, const uint16_t *s1
     const uint64_t n = (uint64_t)T * (uint64_t)H;
     st = check_ptrs(n, {codes1, s1, z1, codes2, s2, z2});
     if (st != FC_OK || n == 0) return st;
-    return from_hip(fc::launch_dequant_sum_requant(codes1, s1, z1, R, n, bits1, bits2, group, g2,
-                                                   codes2, s2, z2, static_cast<hipStream_t>(stream)));
+    return from_hip(run_dsr(codes1, s1, z1, R, n, bits1, bits2, group, g2, codes2, s2, z2,
+                            static_cast<hipStream_t>(stream)));
 }
 
 fc_status fc_dequant_sum_requant(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1,
@@ -126,14 +151,13 @@ fc_status fc_dequant_sum_requant(const uint8_t *codes1, const uint16_t *s1, cons
 fc_status fc_dequantize(const uint8_t *codes2, const uint16_t *s2, const uint16_t *z2,
                         int T, int H, int bits, int group2, fc_dtype dt, void *out, void *stream) {
     if (bits != 4 && bits != 8) return FC_ERR_BITS;
-    if (T < 0 || H < 1 || !pow2_in_range(group2) || H % group2 != 0) return FC_ERR_SHAPE;
+    if (T < 0 || H < 1 || !group_ok(group2) || H % group2 != 0) return FC_ERR_SHAPE;
     if (dt != FC_F16 && dt != FC_BF16) return FC_ERR_DTYPE;
     const uint64_t n = (uint64_t)T * (uint64_t)H;
     fc_status st = check_ptrs(n, {codes2, s2, z2, out});
     if (st != FC_OK || n == 0) return st;
-    return from_hip(fc::launch_dequantize(codes2, s2, z2, n, bits, group2, (int)dt,
-                                          static_cast<uint16_t *>(out),
-                                          static_cast<hipStream_t>(stream)));
+    return from_hip(run_dequantize(codes2, s2, z2, n, bits, group2, dt, nullptr, out,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 fc_status fc_allreduce_emulated_mixed(const void *x, fc_dtype dt, int R, int T, int H, int bits1,
@@ -155,15 +179,13 @@ fc_status fc_dequantize_residual(const uint8_t *codes2, const uint16_t *s2, cons
                                  int T, int H, int bits, int group2, fc_dtype dt,
                                  const void *residual, void *out, void *stream) {
     if (bits != 4 && bits != 8) return FC_ERR_BITS;
-    if (T < 0 || H < 1 || !pow2_in_range(group2) || H % group2 != 0) return FC_ERR_SHAPE;
+    if (T < 0 || H < 1 || !group_ok(group2) || H % group2 != 0) return FC_ERR_SHAPE;
     if (dt != FC_F16 && dt != FC_BF16) return FC_ERR_DTYPE;
     const uint64_t n = (uint64_t)T * (uint64_t)H;
     fc_status st = check_ptrs(n, {codes2, s2, z2, residual, out});
     if (st != FC_OK || n == 0) return st;
-    return from_hip(fc::launch_dequantize_residual(codes2, s2, z2, n, bits, group2, (int)dt,
-                                                   static_cast<const uint16_t *>(residual),
-                                                   static_cast<uint16_t *>(out),
-                                                   static_cast<hipStream_t>(stream)));
+    return from_hip(run_dequantize(codes2, s2, z2, n, bits, group2, dt, residual, out,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 fc_status fc_allreduce_emulated(const void *x, fc_dtype dt, int R, int T, int H, int bits, int group,
@@ -207,7 +229,7 @@ fc_status fc_linear_quantize(const void *a, const void *w, fc_dtype dt, int R, i
     fc_status st = check_shape(R, T, H, bits, group, &g2);
     if (st != FC_OK) return st;
     if (K < kLinearTileK || K % kLinearTileK != 0 || K > kLinearMaxK || H % kLinearTileN != 0 ||
-        H > kLinearMaxH || group > kLinearMaxGroup)
+        H > kLinearMaxH || group > kLinearMaxGroup || !pow2_in_range(group))
         return FC_ERR_SHAPE;
     if (dt != FC_F16 && dt != FC_BF16) return FC_ERR_DTYPE;
     const uint64_t n = (uint64_t)R * (uint64_t)T * (uint64_t)H;

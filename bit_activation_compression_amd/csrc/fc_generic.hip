@@ -1,0 +1,352 @@
+// The three codec kernels for any even group length: the groups the fast
+// kernels do not take (lengths that are not a power of two in [8, 8192], such
+// as 24, 96 or 6144). Same arithmetic as the fast kernels and the method of
+// "Flash Communication: Reducing Tensor Parallelization Bottleneck for Fast
+// Large Language Model Inference" (Figure 5, right; groups along the hidden
+// dimension as in Figure 4), hence the same bits; the layout is simpler.
+//
+// Work layout: a group of G values is P = G/2 pairs (G is even and groups
+// start at even positions, so a pair never straddles two groups, and a 4-bit
+// code pair is one byte). A lane handles pairs:
+//   - P <= 64: each group takes an aligned segment of P2 lanes (P2 the next
+//     power of two >= P), 64/P2 groups per wave; lanes k >= P of a segment
+//     are idle. The group's min/max is reduced over its segment with xor
+//     shuffles of distance 1 .. P2/2, which stay inside the segment.
+//   - P > 64: one group per wave; lane k takes pairs k, k + 64, ...; the
+//     min/max is reduced over the wave, and the values are read a second
+//     time (from the caches) to encode them.
+// Idle lanes contribute +inf / -inf to the reductions.
+#include "fc_device.h"
+#include "fc_launch.h"
+
+namespace fc {
+namespace {
+
+constexpr float kInf = __builtin_inff();
+
+struct PairMap {
+    uint32_t P;          // pairs per group
+    uint32_t p2_shift;   // log2 of the lanes per group segment (P <= 64)
+    bool wide;           // P > 64: one group per wave
+};
+
+// min/max over the lanes of an aligned segment of 2^shift lanes
+__device__ __forceinline__ void segment_minmax(float &mn, float &mx, uint32_t shift) {
+    for (uint32_t d = 1; d < (1u << shift); d <<= 1) {
+        mn = __builtin_fminf(mn, __shfl_xor(mn, (int)d));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, (int)d));
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void widen2(uint32_t w, float &a, float &b) {
+    if constexpr (DT == 1) {
+        a = __builtin_bit_cast(float, w << 16);
+        b = __builtin_bit_cast(float, w & 0xFFFF0000u);
+    } else {
+        const f16x2 h = __builtin_bit_cast(f16x2, w);
+        a = (float)h.x;
+        b = (float)h.y;
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t narrow2(float a, float b) {
+    const f32x2 pair = {as_f32(a), as_f32(b)};
+    if constexpr (DT == 1) return __builtin_bit_cast(uint32_t, __builtin_convertvector(pair, bf16x2));
+    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(pair, f16x2));
+}
+
+// Codes of a pair: q = clamp(round_half_even(fp32(fp32(v - z) * inv)), 0, Q)
+// (v_cvt_pk_u8_f32 rounds to nearest even and saturates to [0, 255]), as
+// one byte of two 4-bit codes (even value in the low nibble) or two bytes.
+template <int BITS>
+__device__ __forceinline__ uint32_t encode2(float a, float b, const GroupParams &p) {
+    const float ta = (a - p.z) * p.inv;
+    const float tb = (b - p.z) * p.inv;
+    const uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(tb, 1, __builtin_amdgcn_cvt_pk_u8_f32(ta, 0, 0u));
+    if constexpr (BITS == 4) {
+        const uint32_t qa = __builtin_elementwise_min(w & 0xFFu, 15u);
+        const uint32_t qb = __builtin_elementwise_min(w >> 8, 15u);
+        return qa | (qb << 4);
+    } else {
+        return w;
+    }
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_pair_codes(uint8_t *codes, uint64_t e, uint32_t c) {
+    if constexpr (BITS == 4) codes[e / 2] = (uint8_t)c;
+    else *reinterpret_cast<uint16_t *>(codes + e) = (uint16_t)c;
+}
+
+template <int BITS>
+__device__ __forceinline__ void load_pair_codes(const uint8_t *codes, uint64_t e, float &qa, float &qb) {
+    if constexpr (BITS == 4) {
+        const uint32_t c = codes[e / 2];
+        qa = (float)(c & 15u);
+        qb = (float)(c >> 4);
+    } else {
+        const uint32_t c = *reinterpret_cast<const uint16_t *>(codes + e);
+        qa = (float)(c & 0xFFu);
+        qb = (float)(c >> 8);
+    }
+}
+
+// Which group and pair this lane handles (P <= 64), or the group of the wave
+// (P > 64). Returns false for a wave wholly past the last group.
+struct Slot {
+    uint64_t group;
+    uint32_t k;        // pair index inside the group (first pair when wide)
+    bool active;       // this lane's pair exists (narrow layout)
+};
+
+__device__ __forceinline__ bool lane_slot(const PairMap &m, uint64_t groups, Slot &s) {
+    const uint64_t wave = wave_index();
+    const uint32_t lane = (uint32_t)lane_id();
+    if (m.wide) {
+        if (wave >= groups) return false;
+        s.group = wave;
+        s.k = lane;
+        s.active = true;
+        return true;
+    }
+    const uint32_t per_wave = kWave >> m.p2_shift;
+    if (wave * per_wave >= groups) return false;
+    s.group = wave * per_wave + (lane >> m.p2_shift);
+    s.k = lane & ((1u << m.p2_shift) - 1u);
+    s.active = s.group < groups && s.k < m.P;
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// stage-1 quantizer: x [n] 16-bit -> codes, s, z in groups of G
+// ---------------------------------------------------------------------------
+template <int DT, int BITS>
+__global__ __launch_bounds__(kBlockThreads) void quantize_generic_kernel(
+    const uint16_t *__restrict__ x, uint64_t n, uint32_t G, PairMap m, uint8_t *__restrict__ codes,
+    uint16_t *__restrict__ s_out, uint16_t *__restrict__ z_out) {
+    const uint64_t groups = n / G;
+    Slot sl;
+    if (!lane_slot(m, groups, sl)) return;
+    const uint64_t base = sl.group * G;
+    const uint32_t *xw = reinterpret_cast<const uint32_t *>(x);
+    if (!m.wide) {
+        float a = kInf, b = kInf, mn = kInf, mx = -kInf;
+        if (sl.active) {
+            widen2<DT>(xw[(base >> 1) + sl.k], a, b);
+            mn = __builtin_fminf(a, b);
+            mx = __builtin_fmaxf(a, b);
+        }
+        segment_minmax(mn, mx, m.p2_shift);
+        const GroupParams p = group_params<BITS>(mn, mx);
+        if (!sl.active) return;
+        store_pair_codes<BITS>(codes, base + 2 * sl.k, encode2<BITS>(a, b, p));
+        if (sl.k == 0) {
+            s_out[sl.group] = p.s16;
+            z_out[sl.group] = p.z16;
+        }
+        return;
+    }
+    float mn = kInf, mx = -kInf;
+    for (uint32_t k = sl.k; k < m.P; k += kWave) {
+        float a, b;
+        widen2<DT>(xw[(base >> 1) + k], a, b);
+        mn = __builtin_fminf(mn, __builtin_fminf(a, b));
+        mx = __builtin_fmaxf(mx, __builtin_fmaxf(a, b));
+    }
+    lanes_minmax<kWave>(mn, mx);
+    const GroupParams p = group_params<BITS>(mn, mx);
+    for (uint32_t k = sl.k; k < m.P; k += kWave) {
+        float a, b;
+        widen2<DT>(xw[(base >> 1) + k], a, b);
+        store_pair_codes<BITS>(codes, base + 2 * k, encode2<BITS>(a, b, p));
+    }
+    if (sl.k == 0) {
+        s_out[sl.group] = p.s16;
+        z_out[sl.group] = p.z16;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Reduce-Scatter reduction + requantization: positions p of n = T*H, stage-1
+// groups of G1 (per operand, operand stride n), stage-2 groups of G2
+// ---------------------------------------------------------------------------
+
+// binary32 sums of the pair of positions (e, e + 1) over the R operands, in
+// ascending r starting from operand 0; each term fp32(q*s + z) (q*s exact)
+template <int BITS1>
+__device__ __forceinline__ void sum_pair(const uint8_t *codes1, const uint16_t *s1,
+                                         const uint16_t *z1, int R, uint64_t n, uint32_t G1,
+                                         uint64_t e, float &ya, float &yb) {
+    const uint64_t per_op = n / G1;   // stage-1 groups per operand (G1 divides n)
+    const uint64_t g = e / G1;
+    for (int r = 0; r < R; ++r) {
+        float qa, qb;
+        load_pair_codes<BITS1>(codes1, (uint64_t)r * n + e, qa, qb);
+        const uint64_t mi = (uint64_t)r * per_op + g;
+        const float s = half_bits_to_float(s1[mi]);
+        const float z = half_bits_to_float(z1[mi]);
+        const float xa = __builtin_fmaf(qa, s, z);
+        const float xb = __builtin_fmaf(qb, s, z);
+        ya = r == 0 ? xa : ya + xa;
+        yb = r == 0 ? xb : yb + xb;
+    }
+}
+
+template <int BITS1, int BITS2>
+__global__ __launch_bounds__(kBlockThreads) void dsr_generic_kernel(
+    const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ s1,
+    const uint16_t *__restrict__ z1, int R, uint64_t n, uint32_t G1, uint32_t G2, PairMap m,
+    uint8_t *__restrict__ codes2, uint16_t *__restrict__ s2, uint16_t *__restrict__ z2) {
+    const uint64_t groups = n / G2;
+    Slot sl;
+    if (!lane_slot(m, groups, sl)) return;
+    const uint64_t base = sl.group * G2;
+    if (!m.wide) {
+        float a = kInf, b = kInf, mn = kInf, mx = -kInf;
+        if (sl.active) {
+            sum_pair<BITS1>(codes1, s1, z1, R, n, G1, base + 2 * sl.k, a, b);
+            mn = __builtin_fminf(a, b);
+            mx = __builtin_fmaxf(a, b);
+        }
+        segment_minmax(mn, mx, m.p2_shift);
+        const GroupParams p = group_params<BITS2>(mn, mx);
+        if (!sl.active) return;
+        store_pair_codes<BITS2>(codes2, base + 2 * sl.k, encode2<BITS2>(a, b, p));
+        if (sl.k == 0) {
+            s2[sl.group] = p.s16;
+            z2[sl.group] = p.z16;
+        }
+        return;
+    }
+    float mn = kInf, mx = -kInf;
+    for (uint32_t k = sl.k; k < m.P; k += kWave) {
+        float a, b;
+        sum_pair<BITS1>(codes1, s1, z1, R, n, G1, base + 2 * k, a, b);
+        mn = __builtin_fminf(mn, __builtin_fminf(a, b));
+        mx = __builtin_fmaxf(mx, __builtin_fmaxf(a, b));
+    }
+    lanes_minmax<kWave>(mn, mx);
+    const GroupParams p = group_params<BITS2>(mn, mx);
+    for (uint32_t k = sl.k; k < m.P; k += kWave) {
+        float a, b;
+        sum_pair<BITS1>(codes1, s1, z1, R, n, G1, base + 2 * k, a, b);
+        store_pair_codes<BITS2>(codes2, base + 2 * k, encode2<BITS2>(a, b, p));
+    }
+    if (sl.k == 0) {
+        s2[sl.group] = p.s16;
+        z2[sl.group] = p.z16;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// final dequantize (+ residual add): one pair of positions per lane
+// ---------------------------------------------------------------------------
+template <int DT, int BITS, bool RES>
+__global__ __launch_bounds__(kBlockThreads) void dequant_generic_kernel(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ s,
+    const uint16_t *__restrict__ z, uint64_t n, uint32_t G2, const uint16_t *res, uint16_t *out) {
+    const uint64_t pair = wave_index() * kWave + (uint64_t)lane_id();
+    const uint64_t e = 2 * pair;
+    if (e >= n) return;
+    float qa, qb;
+    load_pair_codes<BITS>(codes, e, qa, qb);
+    const uint64_t g = e / G2;
+    const float sf = half_bits_to_float(s[g]);
+    const float zf = half_bits_to_float(z[g]);
+    uint32_t o = narrow2<DT>(__builtin_fmaf(qa, sf, zf), __builtin_fmaf(qb, sf, zf));
+    if constexpr (RES) {
+        float a, b, ra, rb;
+        widen2<DT>(o, a, b);   // the all-reduce result as the dtype holds it
+        widen2<DT>(reinterpret_cast<const uint32_t *>(res)[pair], ra, rb);
+        o = narrow2<DT>(ra + a, rb + b);
+    }
+    reinterpret_cast<uint32_t *>(out)[pair] = o;
+}
+
+PairMap pair_map(uint32_t G) {
+    PairMap m;
+    m.P = G / 2;
+    m.wide = m.P > (uint32_t)kWave;
+    m.p2_shift = 0;
+    while (!m.wide && (1u << m.p2_shift) < m.P) ++m.p2_shift;
+    return m;
+}
+
+// workgroups for `groups` groups laid out by m
+hipError_t grid_for(const PairMap &m, uint64_t groups, unsigned *blocks) {
+    const uint64_t per_wave = m.wide ? 1 : (kWave >> m.p2_shift);
+    const uint64_t waves = (groups + per_wave - 1) / per_wave;
+    const uint64_t b = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (b > 0x7FFFFFFFull || b == 0) return hipErrorInvalidConfiguration;
+    *blocks = (unsigned)b;
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_generic(const uint16_t *x, int dtype, uint64_t n, int bits, int group,
+                                   uint8_t *codes, uint16_t *s, uint16_t *z, hipStream_t stream) {
+    const PairMap m = pair_map((uint32_t)group);
+    unsigned blocks = 0;
+    hipError_t e = grid_for(m, n / (uint64_t)group, &blocks);
+    if (e != hipSuccess) return e;
+#define FC_GO(DT, B)                                                                           \
+    hipLaunchKernelGGL((quantize_generic_kernel<DT, B>), dim3(blocks), dim3(kBlockThreads), 0, \
+                       stream, x, n, (uint32_t)group, m, codes, s, z)
+    if (dtype == 0) {
+        if (bits == 4) FC_GO(0, 4);
+        else FC_GO(0, 8);
+    } else {
+        if (bits == 4) FC_GO(1, 4);
+        else FC_GO(1, 8);
+    }
+#undef FC_GO
+    return hipGetLastError();
+}
+
+hipError_t launch_dsr_generic(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1, int R,
+                              uint64_t n, int bits1, int bits2, int group1, int group2,
+                              uint8_t *codes2, uint16_t *s2, uint16_t *z2, hipStream_t stream) {
+    const PairMap m = pair_map((uint32_t)group2);
+    unsigned blocks = 0;
+    hipError_t e = grid_for(m, n / (uint64_t)group2, &blocks);
+    if (e != hipSuccess) return e;
+#define FC_GO(B1, B2)                                                                           \
+    hipLaunchKernelGGL((dsr_generic_kernel<B1, B2>), dim3(blocks), dim3(kBlockThreads), 0, stream, \
+                       codes1, s1, z1, R, n, (uint32_t)group1, (uint32_t)group2, m, codes2, s2, z2)
+    if (bits1 == 4) {
+        if (bits2 == 4) FC_GO(4, 4);
+        else FC_GO(4, 8);
+    } else {
+        if (bits2 == 4) FC_GO(8, 4);
+        else FC_GO(8, 8);
+    }
+#undef FC_GO
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize_generic(const uint8_t *codes2, const uint16_t *s2, const uint16_t *z2,
+                                     uint64_t n, int bits, int group2, int dtype,
+                                     const uint16_t *residual, uint16_t *out, hipStream_t stream) {
+    const uint64_t pairs = n / 2;
+    const uint64_t b = (pairs + kBlockThreads - 1) / kBlockThreads;
+    if (b > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)b);
+#define FC_GO(DT, B, RS)                                                                      \
+    hipLaunchKernelGGL((dequant_generic_kernel<DT, B, RS>), grid, dim3(kBlockThreads), 0,     \
+                       stream, codes2, s2, z2, n, (uint32_t)group2, residual, out)
+    const bool res = residual != nullptr;
+    if (dtype == 0) {
+        if (bits == 4) { if (res) FC_GO(0, 4, true); else FC_GO(0, 4, false); }
+        else { if (res) FC_GO(0, 8, true); else FC_GO(0, 8, false); }
+    } else {
+        if (bits == 4) { if (res) FC_GO(1, 4, true); else FC_GO(1, 4, false); }
+        else { if (res) FC_GO(1, 8, true); else FC_GO(1, 8, false); }
+    }
+#undef FC_GO
+    return hipGetLastError();
+}
+
+}  // namespace fc

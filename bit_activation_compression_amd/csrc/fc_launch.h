@@ -51,6 +51,18 @@ hipError_t launch_allreduce_small(const uint16_t *x, int dtype, int R, uint64_t 
                                   uint16_t *z1, uint8_t *codes2, uint16_t *s2, uint16_t *z2,
                                   const uint16_t *residual, uint16_t *out, hipStream_t stream);
 
+// The same three steps for any even group length (the lengths the launchers
+// above do not take: not a power of two in [8, 8192]); same bits.
+hipError_t launch_quantize_generic(const uint16_t *x, int dtype, uint64_t n, int bits, int group,
+                                   uint8_t *codes, uint16_t *s, uint16_t *z, hipStream_t stream);
+hipError_t launch_dsr_generic(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1, int R,
+                              uint64_t n, int bits1, int bits2, int group1, int group2,
+                              uint8_t *codes2, uint16_t *s2, uint16_t *z2, hipStream_t stream);
+// residual: NULL for the plain dequantize, else the residual add
+hipError_t launch_dequantize_generic(const uint8_t *codes2, const uint16_t *s2, const uint16_t *z2,
+                                     uint64_t n, int bits, int group2, int dtype,
+                                     const uint16_t *residual, uint16_t *out, hipStream_t stream);
+
 // Uncompressed R-way sum over n = T*H positions of R operands laid out [R][n].
 hipError_t launch_sum(const uint16_t *x, int dtype, int R, uint64_t n, uint16_t *out,
                       hipStream_t stream);

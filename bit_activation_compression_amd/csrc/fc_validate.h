@@ -26,7 +26,13 @@ constexpr int kLinearMaxGroup = 256;
 constexpr int kLinearMaxK = 1 << 22;
 constexpr int kLinearMaxH = 1 << 24;
 
+// Group lengths the fast kernels take; any other even length runs on the
+// generic kernels (fc_generic.hip).
 inline bool pow2_in_range(int g) { return g >= kMinGroup && g <= kMaxGroup && (g & (g - 1)) == 0; }
+
+// A group length the codec accepts: even (a 4-bit code pair is one byte, and
+// groups start at even positions) and at least 2.
+inline bool group_ok(int g) { return g >= 2 && g % 2 == 0; }
 
 inline bool aligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -36,11 +42,11 @@ inline size_t round_up(size_t v) { return (v + kSliceAlign - 1) / kSliceAlign * 
 inline fc_status check_shape(int R, int T, int H, int bits, int group, int *g2) {
     if (bits != 4 && bits != 8) return FC_ERR_BITS;
     if (R < 1 || T < 0 || H < 1) return FC_ERR_SHAPE;
-    if (!pow2_in_range(group) || H % group != 0) return FC_ERR_SHAPE;
+    if (!group_ok(group) || H % group != 0) return FC_ERR_SHAPE;
     if (H % R != 0) return FC_ERR_SHAPE;
     const int C = H / R;
     const int g = group < C ? group : C;
-    if (!pow2_in_range(g) || C % g != 0) return FC_ERR_SHAPE;
+    if (!group_ok(g) || C % g != 0) return FC_ERR_SHAPE;
     *g2 = g;
     return FC_OK;
 }

@@ -45,9 +45,11 @@
  *     fc_allreduce_emulated_noalloc on one device.
  *
  * Supported shapes (FC_ERR_SHAPE otherwise): R >= 1, T >= 0, H >= 1,
- * bits in {4, 8} (FC_ERR_BITS), group a power of two in [8, 8192] dividing H,
- * H % R == 0, and the stage-2 group g2 = min(group, H/R) a power of two in
- * [8, 8192] dividing H/R.
+ * bits in {4, 8} (FC_ERR_BITS), group even, at least 2 and dividing H,
+ * H % R == 0, and the stage-2 group g2 = min(group, H/R) even and dividing
+ * H/R. Power-of-two groups in [8, 8192] run on the fast kernels; any other
+ * even length (24, 96, 6144, ...) runs on generic kernels with the same
+ * bits, more slowly.
  */
 #ifndef FC_H_
 #define FC_H_
@@ -102,7 +104,7 @@ fc_status fc_dequant_sum_requant(const uint8_t *codes1, const uint16_t *s1, cons
  * Dequantize after the All-Gather (Figure 5, right).
  *   codes2 [T][H*bits/8], s2, z2 [T][H/group2]  ->  out [T][H] in dt
  * out = round_half_even_to_dt(fp32(q * s + z)).
- * group2 must be a power of two in [8, 8192] dividing H.
+ * group2 must be even and divide H.
  */
 fc_status fc_dequantize(const uint8_t *codes2, const uint16_t *s2, const uint16_t *z2,
                         int T, int H, int bits, int group2, fc_dtype dt, void *out, void *stream);
@@ -182,8 +184,9 @@ fc_status fc_allreduce_emulated_residual(const void *x, fc_dtype dt, int R, int 
  * rounded product by the accumulation error; the codes are always those of
  * the y this call computes (and writes, when y != NULL).
  * Extra requirements (FC_ERR_SHAPE otherwise): K a positive multiple of 32
- * and at most 2^22, H a multiple of 256 and at most 2^24, group <= 256. Same
- * checks as fc_quantize_groups otherwise; y, when given, 16-byte aligned.
+ * and at most 2^22, H a multiple of 256 and at most 2^24, group a power of
+ * two in [8, 256]. Same checks as fc_quantize_groups otherwise; y, when
+ * given, 16-byte aligned.
  */
 fc_status fc_linear_quantize(const void *a, const void *w, fc_dtype dt, int R, int T, int K, int H,
                              int bits, int group, uint8_t *codes1, uint16_t *s1, uint16_t *z1,

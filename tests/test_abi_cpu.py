@@ -64,10 +64,17 @@ def test_stage2_group():
     assert fc.fc_stage2_group(4, 4096, 4096) == 1024
     assert fc.fc_stage2_group(2, 256, 128) == 128
     assert fc.fc_stage2_group(3, 4096, 128) == 0         # H % R != 0
-    assert fc.fc_stage2_group(4, 4096, 96) == 0          # not a power of two
+    assert fc.fc_stage2_group(4, 4096, 96) == 0          # 96 does not divide 4096
+    assert fc.fc_stage2_group(4, 4608, 96) == 96         # any even group dividing H
+    assert fc.fc_stage2_group(3, 576, 96) == 96
+    assert fc.fc_stage2_group(4, 6144, 6144) == 1536     # g > C: the chunk width
+    assert fc.fc_stage2_group(2, 8, 2) == 2
+    assert fc.fc_stage2_group(4, 36, 12) == 0            # g2 = C = 9 is odd
+    assert fc.fc_stage2_group(2, 12, 3) == 0             # odd group
     assert fc.fc_stage2_group(4, 64, 64) == 16
     assert fc.fc_stage2_group(64, 512, 8) == 8
-    assert fc.fc_stage2_group(128, 512, 8) == 0
+    assert fc.fc_stage2_group(128, 512, 8) == 4          # C = 4 < group: the chunk width
+    assert fc.fc_stage2_group(128, 384, 8) == 0          # C = 3: odd
 
 
 def test_workspace_layout_matches_payload_sizes():
@@ -94,14 +101,17 @@ def _q(*args):
 
 @pytest.mark.parametrize("R,T,H,bits,g,status", [
     (4, 8, 512, 5, 128, 3),       # bits
-    (4, 8, 512, 4, 96, 2),        # group not a power of two
-    (4, 8, 512, 4, 4, 2),         # group below 8
-    (4, 8, 512, 4, 16384, 2),     # group above 8192
+    (4, 8, 512, 4, 96, 2),        # group does not divide H
+    (4, 8, 510, 3, 3, 3),         # bits checked first
+    (2, 8, 510, 4, 3, 2),         # odd group
+    (2, 8, 512, 4, 0, 2),         # zero group
+    (4, 8, 512, 4, 16384, 2),     # group above H
+    (4, 8, 36, 4, 12, 2),         # stage-2 group (the chunk, 9) odd
     (4, 8, 512, 4, 1024, 2),      # group does not divide H
     (3, 8, 512, 4, 128, 2),       # H % R
     (0, 8, 512, 4, 128, 2),       # R
     (4, -1, 512, 4, 128, 2),      # T
-    (128, 8, 512, 4, 8, 2),       # C = 4 gives g2 = 4 < 8
+    (128, 8, 384, 4, 8, 2),       # C = 3 gives an odd stage-2 group
 ])
 def test_quantize_rejects_bad_shapes(R, T, H, bits, g, status):
     assert _q(FAKE, 0, R, T, H, bits, g, FAKE, FAKE, FAKE, None) == status
