@@ -455,6 +455,45 @@ def stream_ceilings(torch, fc, dev, stream, nbytes: int) -> dict:
     return out
 
 
+def clock_trace(torch, fc, step, stream, dev, name: str, blocks: int = 80, per_block: int = 10,
+                idle_s: float = COLD_IDLE_S) -> int:
+    """From an idle GPU: `blocks` blocks of `per_block` pipeline steps back to back, the
+    engine clock read with fc_internal_clock_probe after each block (a one-wave kernel,
+    ~2 us), HIP events between blocks. Prints one JSON line: microseconds per step and MHz
+    per block, twice (two idle starts)."""
+    L = fc.lib()
+    probe = L.fc_internal_clock_probe
+    probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    probe.restype = ctypes.c_int
+    buf = torch.zeros((blocks, 4), dtype=torch.int64, device=dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    runs = []
+    for rep in range(2):
+        torch.cuda.synchronize()
+        time.sleep(idle_s)
+        ev = _events(torch, blocks + 1)
+        ev[0].record(stream)
+        for b in range(blocks):
+            for i in range(per_block):
+                step(i)
+            if probe(ctypes.c_void_p(buf[b].data_ptr()), 2000, sp) != 0:
+                raise RuntimeError("fc_internal_clock_probe failed")
+            ev[b + 1].record(stream)
+        torch.cuda.synchronize()
+        c = buf.cpu()
+        mhz = (c[:, 0].double() / c[:, 1].double() * 100.0).tolist()
+        us = [ev[b].elapsed_time(ev[b + 1]) * 1e3 / per_block for b in range(blocks)]
+        runs.append({"us_per_step": [round(u, 1) for u in us], "mhz": [round(m) for m in mhz]})
+        print(f"[clock] start {rep}: first blocks " +
+              " ".join(f"{u:.0f}us/{m:.0f}MHz" for u, m in zip(us[:12], mhz[:12])),
+              file=sys.stderr, flush=True)
+    print(json.dumps({"clock_trace": runs, "workload": name, "steps_per_block": per_block,
+                      "idle_s_before": idle_s,
+                      "note": "each block ends with a one-wave clock probe (~2 us), counted in "
+                              "its time per step"}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -469,6 +508,10 @@ def main() -> int:
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline, its per-kernel pass and the streaming ceilings "
                          "(profiling runs; the ceilings' copy kernel calibrates the counters)")
+    ap.add_argument("--clock-trace", action="store_true",
+                    help="instead of the benchmark: from an idle GPU, run the pipeline in blocks "
+                         "of 10 steps with the engine clock read after each block (the load-onset "
+                         "clock dip the settle phase waits out)")
     ap.add_argument("--quality", action="store_true",
                     help="instead of the benchmark: error (MSE) of both stages and throughput for "
                          "every block size and width of the sweep and for the five workloads")
@@ -531,6 +574,9 @@ def main() -> int:
         fc.fc_dequantize(c2, s2, z2, T, H, bits, g2, tdt, out, stream=stream)
         if ev is not None:
             ev[3].record(stream)
+
+    if args.clock_trace:
+        return clock_trace(torch, fc, step, stream, dev, w.name)
 
     counter = [0]
 

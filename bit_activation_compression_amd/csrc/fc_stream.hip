@@ -1,6 +1,8 @@
-// Streaming probes: the HBM bandwidth a plain kernel reaches for the traffic
-// shapes of the codec's kernels, as the practical ceiling their measured
-// bandwidth is compared with. Not part of the codec.
+// Measurement helpers, not part of the codec. Streaming probes: the HBM
+// bandwidth a plain kernel reaches for the traffic shapes of the codec's
+// kernels, as the practical ceiling their measured bandwidth is compared
+// with. A clock probe: the engine clock the GPU runs at, read between
+// kernels of a running pipeline.
 //
 //   kind 0  copy            read n bytes, write n bytes
 //   kind 1  read 4, write 1 read n bytes, write n/4 bytes (the stage-1
@@ -82,8 +84,34 @@ hipError_t launch_u(int slots, const void *src, void *dst, uint64_t n, hipStream
     }
 }
 
+// One wave: the shader-clock counter (s_memtime) and the constant 100 MHz
+// counter (s_memrealtime) around a chain of `iters` dependent fma, written to
+// out[0] and out[1]; out[2] keeps the chain's result live.
+__global__ void clock_probe_kernel(uint64_t *out, int iters) {
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    float a = (float)lane_id();
+    for (int i = 0; i < iters; ++i) a = __builtin_fmaf(a, 0.999f, 1.0f);
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    if (lane_id() == 0) {
+        out[0] = t1 - t0;
+        out[1] = r1 - r0;
+        out[2] = (uint64_t)__builtin_bit_cast(uint32_t, a);
+    }
+}
+
 }  // namespace
 }  // namespace fc
+
+extern "C" int fc_internal_clock_probe(void *out, int iters, void *stream) {
+    if (out == nullptr) return 1;
+    if (iters < 1 || iters > (1 << 20)) return 2;
+    if ((uintptr_t)out & 7u) return 4;
+    hipLaunchKernelGGL(fc::clock_probe_kernel, dim3(1), dim3(fc::kWave), 0,
+                       static_cast<hipStream_t>(stream), static_cast<uint64_t *>(out), iters);
+    return hipGetLastError() == hipSuccess ? 0 : 6;
+}
 
 extern "C" int fc_internal_stream_probe(int kind, int slots, const void *src, void *dst,
                                         size_t bytes, void *stream) {

@@ -1,8 +1,8 @@
 /*
- * fc_internal.h -- a measurement helper of libfc.so, not part of the codec's
- * interface (include/fc.h). The benchmark uses it to measure the bandwidth
+ * fc_internal.h -- measurement helpers of libfc.so, not part of the codec's
+ * interface (include/fc.h). The benchmark uses them to measure the bandwidth
  * ceiling that plain streaming kernels reach on this GPU for the traffic
- * shapes of the codec's kernels.
+ * shapes of the codec's kernels, and the engine clock while the pipeline runs.
  */
 #ifndef FC_INTERNAL_H_
 #define FC_INTERNAL_H_
@@ -29,6 +29,17 @@ extern "C" {
  */
 int fc_internal_stream_probe(int kind, int slots, const void *src, void *dst, size_t bytes,
                              void *stream);
+
+/*
+ * The engine clock at the point of the stream where it is enqueued: one wave
+ * runs `iters` (1 .. 2^20) dependent fused multiply-adds and writes three
+ * uint64 values to `out` (device pointer, 8-byte aligned, 24 bytes):
+ * out[0] shader-clock cycles elapsed (s_memtime), out[1] ticks of the
+ * constant 100 MHz counter (s_memrealtime) over the same interval, out[2] a
+ * value that keeps the work alive. Clock in MHz = 100 * out[0] / out[1].
+ * Returns 0, or 1 (NULL), 2 (iters out of range), 4 (alignment), 6 (launch).
+ */
+int fc_internal_clock_probe(void *out, int iters, void *stream);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
         assert hasattr(L, n), n
     assert sorted(names) == sorted(fc.EXPORTED_SYMBOLS)
     internal = sorted(set(_declared_functions(HEADERS)) - set(names))
-    assert internal == ["fc_internal_stream_probe"]
+    assert internal == ["fc_internal_clock_probe", "fc_internal_stream_probe"]
     for n in internal:
         assert hasattr(L, n), n
 
@@ -216,3 +216,13 @@ def test_stream_probe_validates():
     assert P(0, 4, MISALIGNED, FAKE, 1024, None) == 4
     assert P(0, 4, FAKE, FAKE, 1000, None) == 4
     assert P(0, 4, None, None, 0, None) == 0
+
+
+def test_clock_probe_validates():
+    L = fc.lib()
+    P = L.fc_internal_clock_probe
+    P.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert P(None, 100, None) == 1
+    assert P(FAKE, 0, None) == 2
+    assert P(FAKE, (1 << 20) + 1, None) == 2
+    assert P(ctypes.c_void_p(0x10004), 100, None) == 4
