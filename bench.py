@@ -54,6 +54,12 @@ PEAK_BF16_TFLOPS = 2500.0   # dense bf16/fp16 matrix-core peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_llama3_70b_prefill_traffic.txt")
 K1_SOURCES = ("bit_activation_compression_amd/csrc/fc_quantize.hip",
               "bit_activation_compression_amd/csrc/fc_device.h")
+K2_COUNTER_FILE = os.path.join(ROOT, "profiles", "dsr_llama3_70b_prefill_counters.md")
+K2_SOURCES = ("bit_activation_compression_amd/csrc/fc_dequant_sum_requant.hip",
+              "bit_activation_compression_amd/csrc/fc_device.h")
+# VALU issue peak of the chip: 256 compute units x 4 SIMDs, one wave64 instruction per
+# SIMD every 4 cycles (16 lanes wide), at 2.4 GHz (non-packed instructions)
+PEAK_VALU_G_WAVE_INSTR = 256 * 4 * 2.4 / 4
 
 BREAKDOWN_STEPS = 50   # steps of the per-kernel event pass
 GRAPH_CALLS = 20       # calls captured per HIP graph in the launch-bound measurements
@@ -97,14 +103,34 @@ def code_only(src: str) -> str:
     return " ".join(src.split())
 
 
-def k1_source_hash() -> str:
-    """Hash of K1's code (comments and layout ignored): the counter summary is
+def source_hash(sources=K1_SOURCES) -> str:
+    """Hash of a kernel's code (comments and layout ignored): a counter summary is
     valid while the code it was measured on is unchanged."""
     h = hashlib.sha256()
-    for rel in K1_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
             h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
+
+
+def k1_source_hash() -> str:
+    return source_hash(K1_SOURCES)
+
+
+def measured_k2_valu(workload: str) -> float | None:
+    """VALU wave-instructions per K2 launch (SQ_INSTS_VALU) from the committed counter
+    summary, if it was taken on this workload and on the current K2 source."""
+    if not os.path.exists(K2_COUNTER_FILE):
+        return None
+    txt = open(K2_COUNTER_FILE).read()
+    m_w = re.search(r"^workload:\s*(\S+)", txt, re.M)
+    m_src = re.search(r"^k2_source_sha256_16:\s*(\S+)", txt, re.M)
+    m_v = re.search(r"^k2_valu_wave_instructions_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    if not m_w or m_w.group(1) != workload or not m_src or not m_v:
+        return None
+    if m_src.group(1) != source_hash(K2_SOURCES):
+        return None
+    return float(m_v.group(1))
 
 
 def measured_traffic(workload: str) -> float | None:
@@ -148,6 +174,28 @@ def host_info() -> dict:
         pass
     info["platform"] = platform.platform()
     return info
+
+
+def kernel_rooflines(mb: dict, k_avg, workload: str) -> dict:
+    """K2 against the VALU issue peak (it is bound by vector-ALU issue, not HBM) and K3
+    against the HBM peak, with the per-kernel event times of the breakdown pass."""
+    valu = measured_k2_valu(workload)
+    k2_s, k3_s = float(k_avg[1]) * 1e-3, float(k_avg[2]) * 1e-3
+    k2 = {"bound": "alu", "unit": "G VALU wave-instructions/s", "peak": PEAK_VALU_G_WAVE_INSTR,
+          "achieved": None, "frac": None, "valu_wave_instructions_per_launch": valu,
+          "hbm_gbps": round(mb["k2"] / k2_s / 1e9, 1),
+          "hbm_frac": round(mb["k2"] / k2_s / 1e9 / PEAK_HBM_GBPS, 4),
+          "note": "instructions: SQ_INSTS_VALU from the committed counter summary (null when it "
+                  "was measured on other K2 code); peak: 256 CUs x 4 SIMDs x 2.4 GHz / 4 cycles per "
+                  "wave64 instruction"}
+    if valu is not None:
+        a = valu / k2_s / 1e9
+        k2.update({"achieved": round(a, 1), "frac": round(a / PEAK_VALU_G_WAVE_INSTR, 4)})
+    a3 = mb["k3"] / k3_s / 1e9
+    k3 = {"bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBPS, "achieved": round(a3, 1),
+          "frac": round(a3 / PEAK_HBM_GBPS, 4)}
+    return {"k2_dequant_sum_requant": k2, "k3_dequantize": k3,
+            "timing": "HIP events of the 50-step per-kernel pass (dispatch gap included)"}
 
 
 def _events(torch, n):
@@ -666,6 +714,7 @@ def main() -> int:
         "pipeline_ms_median_events": round(float(np.median(pipe_ms)), 5),
         "pipeline_ms_p10_p90_events": [round(float(np.percentile(pipe_ms, 10)), 5),
                                        round(float(np.percentile(pipe_ms, 90)), 5)],
+        "kernel_rooflines": kernel_rooflines(mb, k_avg, w.name),
         "input_checksum": {"seed": args.seed, "blake2b_64": x_checksum},
         "link_bytes_per_rank": link_bytes(R, T, H, bits, group, g2),
         "roofline": {"bound": "hbm", "kernel": "k1_quantize", "achieved": round(k1_gbps, 1),

@@ -122,3 +122,18 @@ def test_k1_counter_summary_is_for_the_current_code():
     bench.py reports roofline.traffic); a change to K1's code needs a new
     counter run."""
     assert bench.measured_traffic("llama3_70b_prefill") is not None
+
+
+def test_k2_counter_summary_is_for_the_current_code():
+    """The committed counter summary of K2 (VALU instructions per launch, for its ALU
+    roofline) was measured on K2's current code."""
+    v = bench.measured_k2_valu("llama3_70b_prefill")
+    assert v is not None
+    # 16.2 VALU instructions per output position, 8192 x 8192 positions, 64 lanes
+    assert abs(v * 64 / (8192 * 8192) - 16.19) < 0.05
+    assert bench.measured_k2_valu("decode") is None
+
+
+def test_alu_peak_from_unit_counts():
+    # 256 CUs x 4 SIMDs, a wave64 instruction every 4 cycles, 2.4 GHz
+    assert abs(bench.PEAK_VALU_G_WAVE_INSTR - 614.4) < 1e-9

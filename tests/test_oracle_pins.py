@@ -203,6 +203,35 @@ def test_ramp_gives_codes_equal_to_index(bits):
     assert np.array_equal(_hval(z), As)
 
 
+@pytest.mark.parametrize("bits,g", [(4, 6), (4, 24), (8, 96), (8, 258)])
+def test_ramp_codes_in_groups_that_are_not_powers_of_two(bits, g):
+    """Groups of any even length (here 6, 24, 96, 258 values): each group holds a + k*d for a
+    set of levels k that includes 0 and Q (the rest drawn from [0, Q], any order), so s = d,
+    z = a and every code is its k; the group boundaries and the scale/zero indices follow g."""
+    rng = np.random.default_rng(g)
+    Q = 2 ** bits - 1
+    R, T, G = 2, 3, 4
+    H = g * G
+    x = np.empty((R, T, H))
+    idx = np.empty((R, T, H), dtype=np.int64)
+    ds = np.empty((R, T, G))
+    As = np.empty((R, T, G))
+    for r in range(R):
+        for t in range(T):
+            for k in range(G):
+                d = 2.0 ** int(rng.integers(-8, -3))
+                a = int(rng.integers(-64, 64)) * d
+                lv = np.concatenate([[0, Q], rng.integers(0, Q + 1, size=g - 2)])
+                lv = rng.permutation(lv)
+                x[r, t, k * g:(k + 1) * g] = a + lv * d
+                idx[r, t, k * g:(k + 1) * g] = lv
+                ds[r, t, k], As[r, t, k] = d, a
+    codes, s, z = oracle.quantize_groups(_f16(x), oracle.F16, bits, g)
+    assert np.array_equal(_unpack(codes, bits), idx)
+    assert np.array_equal(_hval(s), ds)
+    assert np.array_equal(_hval(z), As)
+
+
 def test_int4_nibble_order_even_element_low():
     x = _f16(np.arange(16) * 0.125).reshape(1, 1, 16)
     codes, s, z = oracle.quantize_groups(x, oracle.F16, 4, 16)
