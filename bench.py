@@ -449,8 +449,14 @@ def other_workloads(torch, np, fc, synth, seed, dev, stream) -> dict:
                                       v["codes2"], v["s2"], v["z2"], stream=s)
             fc.fc_dequantize(v["codes2"], v["s2"], v["z2"], w.T, w.H, w.bits, g2, tdt, out, stream=s)
 
+        def noalloc(s=stream):
+            fc.fc_allreduce_emulated_noalloc(xd, w.bits, w.group, out, stream=s)
+
         settle_clock(torch, single, stream, min_ms=30.0)
         us_single = timed_calls(torch, single, stream, 200) * 1e3
+        settle_clock(torch, noalloc, stream, min_ms=30.0)
+        us_noalloc = timed_calls(torch, noalloc, stream, 200) * 1e3
+        us_noalloc_graph = graph_us_per_call(torch, noalloc, stream, dev)
         settle_clock(torch, three, stream, min_ms=30.0)
         us_three = timed_calls(torch, three, stream, 200) * 1e3
         us_graph = graph_us_per_call(torch, single, stream, dev)
@@ -460,6 +466,8 @@ def other_workloads(torch, np, fc, synth, seed, dev, stream) -> dict:
                      "us_per_call_single_launch": round(us_single, 2),
                      "us_per_call_in_graph": round(us_graph, 2),
                      "us_per_call_three_launches": round(us_three, 2),
+                     "us_per_call_noalloc": round(us_noalloc, 2),
+                     "us_per_call_noalloc_in_graph": round(us_noalloc_graph, 2),
                      "gbps_single_launch": round(mb / (us_single * 1e-6) / 1e9, 1),
                      "graph_calls_per_replay": GRAPH_CALLS,
                      "timing": "HIP events around 200 back-to-back calls through the Python "

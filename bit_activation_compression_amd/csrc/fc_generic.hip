@@ -5,14 +5,17 @@
 // Large Language Model Inference" (Figure 5, right; groups along the hidden
 // dimension as in Figure 4), hence the same bits; the layout is simpler.
 //
-// Work layout: a group of G values is P = G/2 pairs (G is even and groups
-// start at even positions, so a pair never straddles two groups, and a 4-bit
-// code pair is one byte). A lane handles pairs:
+// Work layout: a group of G values is P units of a lane, a unit being 8
+// consecutive values (one 16-byte vector, the fast kernels' per-lane code
+// paths) when G is a multiple of 8 (for the reduction step: both group
+// lengths), else 2 values. G is even and groups start at multiples of G, so a
+// unit never straddles two groups, and a 4-bit code pair is one byte. A lane
+// handles units:
 //   - P <= 64: each group takes an aligned segment of P2 lanes (P2 the next
 //     power of two >= P), 64/P2 groups per wave; lanes k >= P of a segment
 //     are idle. The group's min/max is reduced over its segment with xor
 //     shuffles of distance 1 .. P2/2, which stay inside the segment.
-//   - P > 64: one group per wave; lane k takes pairs k, k + 64, ...; the
+//   - P > 64: one group per wave; lane k takes units k, k + 64, ...; the
 //     min/max is reduced over the wave, and the values are read a second
 //     time (from the caches) to encode them.
 // Idle lanes contribute +inf / -inf to the reductions.
@@ -25,7 +28,7 @@ namespace {
 constexpr float kInf = __builtin_inff();
 
 struct PairMap {
-    uint32_t P;          // pairs per group
+    uint32_t P;          // lane units (pairs or octets) per group
     uint32_t p2_shift;   // log2 of the lanes per group segment (P <= 64)
     bool wide;           // P > 64: one group per wave
 };
@@ -265,9 +268,180 @@ __global__ __launch_bounds__(kBlockThreads) void dequant_generic_kernel(
     reinterpret_cast<uint32_t *>(out)[pair] = o;
 }
 
-PairMap pair_map(uint32_t G) {
+// ---------------------------------------------------------------------------
+// groups whose length is a multiple of 8: a lane takes 8 consecutive values
+// (one 16-byte vector, the fast kernels' per-lane helpers), a group of G
+// values is L8 = G/8 lanes; the same segment layout as the pairs above with
+// octets in place of pairs (a PairMap whose P counts octets)
+// ---------------------------------------------------------------------------
+
+// q = a / d for 64-bit a, with 32-bit division when a fits
+__device__ __forceinline__ uint64_t div_u64(uint64_t a, uint32_t d) {
+    return (a >> 32) == 0 ? (uint64_t)((uint32_t)a / d) : a / d;
+}
+
+template <int DT, int BITS>
+__global__ __launch_bounds__(kBlockThreads) void quantize_oct_kernel(
+    const uint16_t *__restrict__ x, uint64_t n, uint32_t G, PairMap m, uint8_t *__restrict__ codes,
+    uint16_t *__restrict__ s_out, uint16_t *__restrict__ z_out) {
+    constexpr int W = BITS == 4 ? 1 : 2;
+    const uint64_t groups = n / G;
+    Slot sl;
+    if (!lane_slot(m, groups, sl)) return;
+    const uint64_t base = sl.group * G;
+    const uint16_t *xg = x + base;
+    uint8_t *cg = codes + base * BITS / 8;
+    if (!m.wide) {
+        float v[kLaneElems];
+        float mn = kInf, mx = -kInf;
+        if (sl.active) {
+            widen8<DT>(ldv<u32x4, true>(xg, sl.k * 16u), v);
+            minmax8(v, mn, mx);
+        }
+        segment_minmax(mn, mx, m.p2_shift);
+        const GroupParams p = group_params<BITS>(mn, mx);
+        if (!sl.active) return;
+        uint32_t w[W];
+        encode8<BITS>(v, p, w);
+        store_codes<BITS, true>(cg, sl.k * kLaneElems, w);
+        if (sl.k == 0) {
+            s_out[sl.group] = p.s16;
+            z_out[sl.group] = p.z16;
+        }
+        return;
+    }
+    float mn = kInf, mx = -kInf;
+    for (uint32_t k = sl.k; k < m.P; k += kWave) {
+        float v[kLaneElems], a, b;
+        widen8<DT>(ldv<u32x4, true>(xg, k * 16u), v);
+        minmax8(v, a, b);
+        mn = __builtin_fminf(mn, a);
+        mx = __builtin_fmaxf(mx, b);
+    }
+    lanes_minmax<kWave>(mn, mx);
+    const GroupParams p = group_params<BITS>(mn, mx);
+    for (uint32_t k = sl.k; k < m.P; k += kWave) {
+        float v[kLaneElems];
+        widen8<DT>(ldv<u32x4, true>(xg, k * 16u), v);
+        uint32_t w[W];
+        encode8<BITS>(v, p, w);
+        store_codes<BITS, true>(cg, k * kLaneElems, w);
+    }
+    if (sl.k == 0) {
+        s_out[sl.group] = p.s16;
+        z_out[sl.group] = p.z16;
+    }
+}
+
+// binary32 sums of the 8 positions [e, e + 8) over the R operands (ascending r,
+// from operand 0; each term fp32(q*s + z), the product exact); g1 = e / G1,
+// the stage-1 group of the octet (G1 is a multiple of 8, so one group)
+template <int BITS1>
+__device__ __forceinline__ void sum_oct(const uint8_t *codes1, const uint16_t *s1,
+                                        const uint16_t *z1, int R, uint64_t n, uint64_t per_op,
+                                        uint64_t g1, uint64_t e, float (&y)[kLaneElems]) {
+    for (int r = 0; r < R; ++r) {
+        uint32_t w[BITS1 == 4 ? 1 : 2];
+        load_codes<BITS1, false>(codes1 + ((uint64_t)r * n + e) * BITS1 / 8, 0, w);
+        const uint64_t mi = (uint64_t)r * per_op + g1;
+        float xh[kLaneElems];
+        dequant8<BITS1>(w, s1[mi], z1[mi], xh);
+#pragma unroll
+        for (int i = 0; i < kLaneElems; ++i) y[i] = r == 0 ? xh[i] : y[i] + xh[i];
+    }
+}
+
+template <int BITS1, int BITS2>
+__global__ __launch_bounds__(kBlockThreads) void dsr_oct_kernel(
+    const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ s1,
+    const uint16_t *__restrict__ z1, int R, uint64_t n, uint32_t G1, uint32_t G2, PairMap m,
+    uint8_t *__restrict__ codes2, uint16_t *__restrict__ s2, uint16_t *__restrict__ z2) {
+    constexpr int W = BITS2 == 4 ? 1 : 2;
+    const uint64_t groups = n / G2;
+    const uint64_t per_op = n / G1;
+    Slot sl;
+    if (!lane_slot(m, groups, sl)) return;
+    const uint64_t base = sl.group * G2;
+    uint8_t *cg = codes2 + base * BITS2 / 8;
+    // the stage-1 group of position e: the stage-2 group itself when G1 == G2
+    auto g1_of = [&](uint64_t e) { return G1 == G2 ? sl.group : div_u64(e, G1); };
+    if (!m.wide) {
+        float y[kLaneElems];
+        float mn = kInf, mx = -kInf;
+        if (sl.active) {
+            const uint64_t e = base + (uint64_t)sl.k * kLaneElems;
+            sum_oct<BITS1>(codes1, s1, z1, R, n, per_op, g1_of(e), e, y);
+            minmax8(y, mn, mx);
+        }
+        segment_minmax(mn, mx, m.p2_shift);
+        const GroupParams p = group_params<BITS2>(mn, mx);
+        if (!sl.active) return;
+        uint32_t w[W];
+        encode8<BITS2>(y, p, w);
+        store_codes<BITS2, false>(cg, sl.k * kLaneElems, w);
+        if (sl.k == 0) {
+            s2[sl.group] = p.s16;
+            z2[sl.group] = p.z16;
+        }
+        return;
+    }
+    float mn = kInf, mx = -kInf;
+    for (uint32_t k = sl.k; k < m.P; k += kWave) {
+        const uint64_t e = base + (uint64_t)k * kLaneElems;
+        float y[kLaneElems], a, b;
+        sum_oct<BITS1>(codes1, s1, z1, R, n, per_op, g1_of(e), e, y);
+        minmax8(y, a, b);
+        mn = __builtin_fminf(mn, a);
+        mx = __builtin_fmaxf(mx, b);
+    }
+    lanes_minmax<kWave>(mn, mx);
+    const GroupParams p = group_params<BITS2>(mn, mx);
+    for (uint32_t k = sl.k; k < m.P; k += kWave) {
+        const uint64_t e = base + (uint64_t)k * kLaneElems;
+        float y[kLaneElems];
+        sum_oct<BITS1>(codes1, s1, z1, R, n, per_op, g1_of(e), e, y);
+        uint32_t w[W];
+        encode8<BITS2>(y, p, w);
+        store_codes<BITS2, false>(cg, k * kLaneElems, w);
+    }
+    if (sl.k == 0) {
+        s2[sl.group] = p.s16;
+        z2[sl.group] = p.z16;
+    }
+}
+
+// one octet of positions per lane
+template <int DT, int BITS, bool RES>
+__global__ __launch_bounds__(kBlockThreads) void dequant_oct_kernel(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ s,
+    const uint16_t *__restrict__ z, uint64_t n, uint32_t G2, const uint16_t *res, uint16_t *out) {
+    const uint64_t e = (wave_index() * kWave + (uint64_t)lane_id()) * kLaneElems;
+    if (e >= n) return;
+    uint32_t w[BITS == 4 ? 1 : 2];
+    load_codes<BITS, false>(codes + e * BITS / 8, 0, w);
+    const uint64_t g = div_u64(e, G2);
+    float q[kLaneElems], o[kLaneElems];
+    decode8<BITS>(w, q);
+    const float sf = half_bits_to_float(s[g]);
+    const float zf = half_bits_to_float(z[g]);
+#pragma unroll
+    for (int k = 0; k < kLaneElems; ++k) o[k] = __builtin_fmaf(q[k], sf, zf);   // exact product
+    u32x4 packed = narrow8<DT>(o);
+    if constexpr (RES) {
+        float a[kLaneElems], r[kLaneElems];
+        widen8<DT>(packed, a);   // the all-reduce result as the dtype holds it
+        widen8<DT>(ldv<u32x4, true>(res + e, 0), r);
+#pragma unroll
+        for (int k = 0; k < kLaneElems; ++k) a[k] = r[k] + a[k];
+        packed = narrow8<DT>(a);
+    }
+    stv<u32x4, true>(out + e, 0, packed);
+}
+
+// unit: the values a lane takes at a time (2, or 8 for the octet kernels)
+PairMap pair_map(uint32_t G, uint32_t unit) {
     PairMap m;
-    m.P = G / 2;
+    m.P = G / unit;
     m.wide = m.P > (uint32_t)kWave;
     m.p2_shift = 0;
     while (!m.wide && (1u << m.p2_shift) < m.P) ++m.p2_shift;
@@ -288,13 +462,21 @@ hipError_t grid_for(const PairMap &m, uint64_t groups, unsigned *blocks) {
 
 hipError_t launch_quantize_generic(const uint16_t *x, int dtype, uint64_t n, int bits, int group,
                                    uint8_t *codes, uint16_t *s, uint16_t *z, hipStream_t stream) {
-    const PairMap m = pair_map((uint32_t)group);
+    const bool oct = group % kLaneElems == 0;
+    const PairMap m = pair_map((uint32_t)group, oct ? kLaneElems : 2);
     unsigned blocks = 0;
     hipError_t e = grid_for(m, n / (uint64_t)group, &blocks);
     if (e != hipSuccess) return e;
-#define FC_GO(DT, B)                                                                           \
-    hipLaunchKernelGGL((quantize_generic_kernel<DT, B>), dim3(blocks), dim3(kBlockThreads), 0, \
-                       stream, x, n, (uint32_t)group, m, codes, s, z)
+#define FC_GO(DT, B)                                                                              \
+    do {                                                                                          \
+        if (oct)                                                                                  \
+            hipLaunchKernelGGL((quantize_oct_kernel<DT, B>), dim3(blocks), dim3(kBlockThreads),   \
+                               0, stream, x, n, (uint32_t)group, m, codes, s, z);                 \
+        else                                                                                      \
+            hipLaunchKernelGGL((quantize_generic_kernel<DT, B>), dim3(blocks),                    \
+                               dim3(kBlockThreads), 0, stream, x, n, (uint32_t)group, m, codes,   \
+                               s, z);                                                             \
+    } while (0)
     if (dtype == 0) {
         if (bits == 4) FC_GO(0, 4);
         else FC_GO(0, 8);
@@ -309,13 +491,22 @@ hipError_t launch_quantize_generic(const uint16_t *x, int dtype, uint64_t n, int
 hipError_t launch_dsr_generic(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1, int R,
                               uint64_t n, int bits1, int bits2, int group1, int group2,
                               uint8_t *codes2, uint16_t *s2, uint16_t *z2, hipStream_t stream) {
-    const PairMap m = pair_map((uint32_t)group2);
+    const bool oct = group1 % kLaneElems == 0 && group2 % kLaneElems == 0;
+    const PairMap m = pair_map((uint32_t)group2, oct ? kLaneElems : 2);
     unsigned blocks = 0;
     hipError_t e = grid_for(m, n / (uint64_t)group2, &blocks);
     if (e != hipSuccess) return e;
-#define FC_GO(B1, B2)                                                                           \
-    hipLaunchKernelGGL((dsr_generic_kernel<B1, B2>), dim3(blocks), dim3(kBlockThreads), 0, stream, \
-                       codes1, s1, z1, R, n, (uint32_t)group1, (uint32_t)group2, m, codes2, s2, z2)
+#define FC_GO(B1, B2)                                                                              \
+    do {                                                                                           \
+        if (oct)                                                                                   \
+            hipLaunchKernelGGL((dsr_oct_kernel<B1, B2>), dim3(blocks), dim3(kBlockThreads), 0,     \
+                               stream, codes1, s1, z1, R, n, (uint32_t)group1, (uint32_t)group2,   \
+                               m, codes2, s2, z2);                                                 \
+        else                                                                                       \
+            hipLaunchKernelGGL((dsr_generic_kernel<B1, B2>), dim3(blocks), dim3(kBlockThreads),    \
+                               0, stream, codes1, s1, z1, R, n, (uint32_t)group1,                  \
+                               (uint32_t)group2, m, codes2, s2, z2);                               \
+    } while (0)
     if (bits1 == 4) {
         if (bits2 == 4) FC_GO(4, 4);
         else FC_GO(4, 8);
@@ -330,13 +521,20 @@ hipError_t launch_dsr_generic(const uint8_t *codes1, const uint16_t *s1, const u
 hipError_t launch_dequantize_generic(const uint8_t *codes2, const uint16_t *s2, const uint16_t *z2,
                                      uint64_t n, int bits, int group2, int dtype,
                                      const uint16_t *residual, uint16_t *out, hipStream_t stream) {
-    const uint64_t pairs = n / 2;
-    const uint64_t b = (pairs + kBlockThreads - 1) / kBlockThreads;
+    const bool oct = group2 % kLaneElems == 0;
+    const uint64_t lanes = n / (oct ? kLaneElems : 2);
+    const uint64_t b = (lanes + kBlockThreads - 1) / kBlockThreads;
     if (b > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)b);
 #define FC_GO(DT, B, RS)                                                                      \
-    hipLaunchKernelGGL((dequant_generic_kernel<DT, B, RS>), grid, dim3(kBlockThreads), 0,     \
-                       stream, codes2, s2, z2, n, (uint32_t)group2, residual, out)
+    do {                                                                                      \
+        if (oct)                                                                              \
+            hipLaunchKernelGGL((dequant_oct_kernel<DT, B, RS>), grid, dim3(kBlockThreads), 0, \
+                               stream, codes2, s2, z2, n, (uint32_t)group2, residual, out);   \
+        else                                                                                  \
+            hipLaunchKernelGGL((dequant_generic_kernel<DT, B, RS>), grid, dim3(kBlockThreads), \
+                               0, stream, codes2, s2, z2, n, (uint32_t)group2, residual, out); \
+    } while (0)
     const bool res = residual != nullptr;
     if (dtype == 0) {
         if (bits == 4) { if (res) FC_GO(0, 4, true); else FC_GO(0, 4, false); }

@@ -7,10 +7,11 @@ g2 = min(group, H/R) is even and divides H/R: "Flash Communication: Reducing
 Tensor Parallelization Bottleneck for Fast Large Language Model Inference",
 Figure 4 (block-wise quantization along the hidden dimension) and Figure 5,
 right (quantization before the Reduce-Scatter and before the All-Gather).
-Cases cover both generic layouts (groups of at most 128 values sharing a
-wave, longer groups one per wave), power-of-two groups below 8 and above
-8192, stage-1 groups on the fast kernel with a stage-2 group on the generic
-one, mixed widths, ragged token counts, R = 1 .. 8, the residual add, edge
+Cases cover both lane units (8 values when the group lengths are multiples
+of 8, else 2) in both layouts (groups of at most 64 units sharing a wave,
+longer groups one per wave), mixed units between the two stages,
+power-of-two groups below 8 and above 8192, stage-1 groups on the fast
+kernel with a stage-2 group on the generic one, mixed widths, ragged token counts, R = 1 .. 8, the residual add, edge
 values, T = 0, and a random sample of shapes. Inputs: the seeded generator.
 """
 from __future__ import annotations
@@ -97,6 +98,10 @@ CASES = [  # R, T, H, bits1, bits2, group, dtype
     (1, 2, 16384, 4, 4, 16384, synth.F16),   # power of two above 8192, R = 1
     (4, 1, 6144, 8, 8, 3072, synth.BF16),    # g > C = 1536, one token
     (6, 11, 1152, 4, 4, 12, synth.F16),      # R = 6, ragged tokens
+    (4, 5, 48, 4, 4, 24, synth.F16),         # stage 1 in octets, stage 2 (12) in pairs
+    (4, 3, 48, 8, 4, 16, synth.BF16),        # stage 1 fast (16), stage 2 (12) in pairs
+    (3, 4, 24, 4, 8, 12, synth.F16),         # stage 1 in pairs, stage 2 fast (8)
+    (2, 7, 1040, 8, 8, 520, synth.BF16),     # 65 octets: one group per wave
 ]
 
 

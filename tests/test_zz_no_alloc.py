@@ -87,3 +87,36 @@ def test_noalloc_largest_shape_fits_and_next_is_rejected():
     assert e.value.status == 8
     torch.cuda.synchronize()
     assert bool((out2 == 3.0).all())
+
+
+@pytest.mark.parametrize("name,kw", [("decode", {}), ("llama3_8b_prefill", {"T": 1100})])
+def test_noalloc_captured_in_a_graph(name, kw):
+    """The callers this entry point is for capture it in HIP graphs: every replay reproduces
+    the eager result, also after an eager call of another shape has overwritten the shared
+    scratch in between (each call writes its payloads before it reads them)."""
+    w = synth.workload(name).with_(**kw)
+    print(f"[noalloc] graph capture {name} R={w.R} T={w.T} H={w.H}", flush=True)
+    _, xd = _x(w, 5)
+    ref, _ = fc.fc_allreduce_emulated(xd, w.bits, w.group)
+    torch.cuda.synchronize()
+    want = _bits(ref)
+    out = torch.empty_like(ref)
+    other_w = synth.workload("tiny")
+    _, xo = _x(other_w, 6)
+    out_o = torch.empty((other_w.T, other_w.H), dtype=xo.dtype, device=DEV)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        fc.fc_allreduce_emulated_noalloc(xd, w.bits, w.group, out, stream=cap)
+        with torch.cuda.graph(graph, stream=cap):
+            fc.fc_allreduce_emulated_noalloc(xd, w.bits, w.group, out, stream=cap)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.zero_()
+        fc.fc_allreduce_emulated_noalloc(xo, other_w.bits, other_w.group, out_o)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(out), want), f"replay {i}"
