@@ -477,8 +477,9 @@ def other_workloads(torch, np, fc, synth, seed, dev, stream) -> dict:
 
 
 def stream_ceilings(torch, fc, dev, stream, nbytes: int) -> dict:
-    """GB/s of the library's plain streaming kernels over nbytes of source (the best of 1, 2,
-    4 and 8 loads in flight per lane): copy, read 4 / write 1 (K1's shape), read only."""
+    """GB/s of the library's plain streaming kernels (the best of 1, 2, 4 and 8 loads in
+    flight per lane): copy, read 4 / write 1 (K1's shape) and read only over nbytes of
+    source, and read 1 / write 4 (K3's shape) over nbytes / 4 of source (nbytes written)."""
     L = fc.lib()
     probe = L.fc_internal_stream_probe
     probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
@@ -488,15 +489,16 @@ def stream_ceilings(torch, fc, dev, stream, nbytes: int) -> dict:
     src.random_(0, 256)
     dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
-    moved = {0: 2 * nbytes, 1: nbytes + nbytes // 4, 2: nbytes}
-    names = {0: "copy", 1: "read4_write1", 2: "read"}
+    src_bytes = {0: nbytes, 1: nbytes, 2: nbytes, 3: nbytes // 4}
+    moved = {0: 2 * nbytes, 1: nbytes + nbytes // 4, 2: nbytes, 3: nbytes // 4 + nbytes}
+    names = {0: "copy", 1: "read4_write1", 2: "read", 3: "read1_write4"}
     out = {}
-    for kind in (0, 1, 2):
+    for kind in (0, 1, 2, 3):
         best = None
         for slots in (1, 2, 4, 8):
             def run(kind=kind, slots=slots):
                 rc = probe(kind, slots, ctypes.c_void_p(src.data_ptr()),
-                           ctypes.c_void_p(dst.data_ptr()), nbytes, sp)
+                           ctypes.c_void_p(dst.data_ptr()), src_bytes[kind], sp)
                 if rc != 0:
                     raise RuntimeError(f"fc_internal_stream_probe returned {rc}")
             settle_clock(torch, run, stream, min_ms=20.0)
@@ -740,6 +742,8 @@ def main() -> int:
     print("[bench] streaming ceilings", file=sys.stderr, flush=True)
     ceil = stream_ceilings(torch, fc, dev, stream, R * T * H * 2)
     ceil["k1_frac_of_read4_write1"] = round(k1_gbps / ceil["read4_write1"]["gbps"], 4)
+    ceil["k3_frac_of_read1_write4"] = round(rec["kernel_gbps"]["k3_dequantize"]
+                                            / ceil["read1_write4"]["gbps"], 4)
     rec["stream_ceilings_gbps"] = ceil
 
     if not args.no_extras:

@@ -5,12 +5,17 @@
 // Large Language Model Inference" (Figure 5, right; groups along the hidden
 // dimension as in Figure 4), hence the same bits; the layout is simpler.
 //
-// Work layout: a group of G values is P units of a lane, a unit being 8
-// consecutive values (one 16-byte vector, the fast kernels' per-lane code
-// paths) when G is a multiple of 8 (for the reduction step: both group
-// lengths), else 2 values. G is even and groups start at multiples of G, so a
-// unit never straddles two groups, and a 4-bit code pair is one byte. A lane
-// handles units:
+// Work layout: a group of G values is P units of a lane. When G is a
+// multiple of 8 (for the reduction step: both group lengths), a unit is M
+// 8-value vectors (16 bytes of 16-bit values each, the fast kernels' per-lane
+// code paths), interleaved over the group's lanes: lane k of P takes vectors
+// k, k + P, ..., k + (M-1) P, so that each load instruction reads runs of
+// 16 P contiguous bytes. M is G/8P with P the largest power of two dividing
+// G/8, at most 64, when that M is 3, 5, 6, 7, 10 or 12 and P >= 4 (groups of
+// 96, 160, 192, 224, 1536, 5120, 6144 ...), else M = 1. Other groups take
+// units of 2 consecutive values. G is even and groups start at multiples of
+// G, so a unit never straddles two groups, and a 4-bit code pair is one
+// byte. A lane handles units:
 //   - P <= 64: each group takes an aligned segment of P2 lanes (P2 the next
 //     power of two >= P), 64/P2 groups per wave; lanes k >= P of a segment
 //     are idle. The group's min/max is reduced over its segment with xor
@@ -28,7 +33,7 @@ namespace {
 constexpr float kInf = __builtin_inff();
 
 struct PairMap {
-    uint32_t P;          // lane units (pairs or octets) per group
+    uint32_t P;          // lane units per group
     uint32_t p2_shift;   // log2 of the lanes per group segment (P <= 64)
     bool wide;           // P > 64: one group per wave
 };
@@ -122,14 +127,32 @@ __device__ __forceinline__ bool lane_slot(const PairMap &m, uint64_t groups, Slo
     return true;
 }
 
+// Quotient n / d of 32-bit values by a multiply-high (the round-up method of
+// T. Granlund and P. Montgomery, "Division by invariant integers using
+// multiplication", 1994): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, t = mulhi(m, n) and
+// q = (t + ((n - t) >> 1)) >> (l - 1), for every n < 2^32 and d >= 2.
+// Positions past 2^32 - 1 (`wide`) divide in 64 bits instead.
+struct GroupDiv {
+    uint32_t d, m, l1;
+    bool wide;
+};
+
+__device__ __forceinline__ uint64_t group_of(uint64_t e, const GroupDiv &D) {
+    if (D.wide) return e / D.d;
+    const uint32_t n = (uint32_t)e;
+    const uint32_t t = __umulhi(D.m, n);
+    return (t + ((n - t) >> 1)) >> D.l1;
+}
+
 // ---------------------------------------------------------------------------
-// stage-1 quantizer: x [n] 16-bit -> codes, s, z in groups of G
+// stage-1 quantizer: x [n] 16-bit -> codes, s, z in `groups` groups of G
+// (units of 2 values)
 // ---------------------------------------------------------------------------
 template <int DT, int BITS>
 __global__ __launch_bounds__(kBlockThreads) void quantize_generic_kernel(
-    const uint16_t *__restrict__ x, uint64_t n, uint32_t G, PairMap m, uint8_t *__restrict__ codes,
-    uint16_t *__restrict__ s_out, uint16_t *__restrict__ z_out) {
-    const uint64_t groups = n / G;
+    const uint16_t *__restrict__ x, uint64_t groups, uint32_t G, PairMap m,
+    uint8_t *__restrict__ codes, uint16_t *__restrict__ s_out, uint16_t *__restrict__ z_out) {
     Slot sl;
     if (!lane_slot(m, groups, sl)) return;
     const uint64_t base = sl.group * G;
@@ -173,17 +196,17 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_generic_kernel(
 
 // ---------------------------------------------------------------------------
 // Reduce-Scatter reduction + requantization: positions p of n = T*H, stage-1
-// groups of G1 (per operand, operand stride n), stage-2 groups of G2
+// groups of G1 (per operand, operand stride n; `per_op` = n / G1 of them),
+// stage-2 groups of G2 (`groups` = n / G2); D1 divides by G1
 // ---------------------------------------------------------------------------
 
 // binary32 sums of the pair of positions (e, e + 1) over the R operands, in
 // ascending r starting from operand 0; each term fp32(q*s + z) (q*s exact)
 template <int BITS1>
 __device__ __forceinline__ void sum_pair(const uint8_t *codes1, const uint16_t *s1,
-                                         const uint16_t *z1, int R, uint64_t n, uint32_t G1,
-                                         uint64_t e, float &ya, float &yb) {
-    const uint64_t per_op = n / G1;   // stage-1 groups per operand (G1 divides n)
-    const uint64_t g = e / G1;
+                                         const uint16_t *z1, int R, uint64_t n, uint64_t per_op,
+                                         const GroupDiv &D1, uint64_t e, float &ya, float &yb) {
+    const uint64_t g = group_of(e, D1);
     for (int r = 0; r < R; ++r) {
         float qa, qb;
         load_pair_codes<BITS1>(codes1, (uint64_t)r * n + e, qa, qb);
@@ -200,16 +223,16 @@ __device__ __forceinline__ void sum_pair(const uint8_t *codes1, const uint16_t *
 template <int BITS1, int BITS2>
 __global__ __launch_bounds__(kBlockThreads) void dsr_generic_kernel(
     const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ s1,
-    const uint16_t *__restrict__ z1, int R, uint64_t n, uint32_t G1, uint32_t G2, PairMap m,
-    uint8_t *__restrict__ codes2, uint16_t *__restrict__ s2, uint16_t *__restrict__ z2) {
-    const uint64_t groups = n / G2;
+    const uint16_t *__restrict__ z1, int R, uint64_t n, uint64_t per_op, GroupDiv D1,
+    uint64_t groups, uint32_t G2, PairMap m, uint8_t *__restrict__ codes2,
+    uint16_t *__restrict__ s2, uint16_t *__restrict__ z2) {
     Slot sl;
     if (!lane_slot(m, groups, sl)) return;
     const uint64_t base = sl.group * G2;
     if (!m.wide) {
         float a = kInf, b = kInf, mn = kInf, mx = -kInf;
         if (sl.active) {
-            sum_pair<BITS1>(codes1, s1, z1, R, n, G1, base + 2 * sl.k, a, b);
+            sum_pair<BITS1>(codes1, s1, z1, R, n, per_op, D1, base + 2 * sl.k, a, b);
             mn = __builtin_fminf(a, b);
             mx = __builtin_fmaxf(a, b);
         }
@@ -226,7 +249,7 @@ __global__ __launch_bounds__(kBlockThreads) void dsr_generic_kernel(
     float mn = kInf, mx = -kInf;
     for (uint32_t k = sl.k; k < m.P; k += kWave) {
         float a, b;
-        sum_pair<BITS1>(codes1, s1, z1, R, n, G1, base + 2 * k, a, b);
+        sum_pair<BITS1>(codes1, s1, z1, R, n, per_op, D1, base + 2 * k, a, b);
         mn = __builtin_fminf(mn, __builtin_fminf(a, b));
         mx = __builtin_fmaxf(mx, __builtin_fmaxf(a, b));
     }
@@ -234,7 +257,7 @@ __global__ __launch_bounds__(kBlockThreads) void dsr_generic_kernel(
     const GroupParams p = group_params<BITS2>(mn, mx);
     for (uint32_t k = sl.k; k < m.P; k += kWave) {
         float a, b;
-        sum_pair<BITS1>(codes1, s1, z1, R, n, G1, base + 2 * k, a, b);
+        sum_pair<BITS1>(codes1, s1, z1, R, n, per_op, D1, base + 2 * k, a, b);
         store_pair_codes<BITS2>(codes2, base + 2 * k, encode2<BITS2>(a, b, p));
     }
     if (sl.k == 0) {
@@ -244,18 +267,19 @@ __global__ __launch_bounds__(kBlockThreads) void dsr_generic_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// final dequantize (+ residual add): one pair of positions per lane
+// final dequantize (+ residual add): one pair of positions per lane; D2
+// divides by G2
 // ---------------------------------------------------------------------------
 template <int DT, int BITS, bool RES>
 __global__ __launch_bounds__(kBlockThreads) void dequant_generic_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ s,
-    const uint16_t *__restrict__ z, uint64_t n, uint32_t G2, const uint16_t *res, uint16_t *out) {
+    const uint16_t *__restrict__ z, uint64_t n, GroupDiv D2, const uint16_t *res, uint16_t *out) {
     const uint64_t pair = wave_index() * kWave + (uint64_t)lane_id();
     const uint64_t e = 2 * pair;
     if (e >= n) return;
     float qa, qb;
     load_pair_codes<BITS>(codes, e, qa, qb);
-    const uint64_t g = e / G2;
+    const uint64_t g = group_of(e, D2);
     const float sf = half_bits_to_float(s[g]);
     const float zf = half_bits_to_float(z[g]);
     uint32_t o = narrow2<DT>(__builtin_fmaf(qa, sf, zf), __builtin_fmaf(qb, sf, zf));
@@ -269,41 +293,53 @@ __global__ __launch_bounds__(kBlockThreads) void dequant_generic_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// groups whose length is a multiple of 8: a lane takes 8 consecutive values
-// (one 16-byte vector, the fast kernels' per-lane helpers), a group of G
-// values is L8 = G/8 lanes; the same segment layout as the pairs above with
-// octets in place of pairs (a PairMap whose P counts octets)
+// groups whose length is a multiple of 8: a lane unit is M consecutive
+// 8-value vectors (see the top of the file); a PairMap whose P counts units
 // ---------------------------------------------------------------------------
 
-// q = a / d for 64-bit a, with 32-bit division when a fits
-__device__ __forceinline__ uint64_t div_u64(uint64_t a, uint32_t d) {
-    return (a >> 32) == 0 ? (uint64_t)((uint32_t)a / d) : a / d;
-}
-
-template <int DT, int BITS>
+template <int DT, int BITS, int M>
 __global__ __launch_bounds__(kBlockThreads) void quantize_oct_kernel(
-    const uint16_t *__restrict__ x, uint64_t n, uint32_t G, PairMap m, uint8_t *__restrict__ codes,
-    uint16_t *__restrict__ s_out, uint16_t *__restrict__ z_out) {
+    const uint16_t *__restrict__ x, uint64_t groups, uint32_t G, PairMap m,
+    uint8_t *__restrict__ codes, uint16_t *__restrict__ s_out, uint16_t *__restrict__ z_out) {
     constexpr int W = BITS == 4 ? 1 : 2;
-    const uint64_t groups = n / G;
     Slot sl;
     if (!lane_slot(m, groups, sl)) return;
     const uint64_t base = sl.group * G;
     const uint16_t *xg = x + base;
     uint8_t *cg = codes + base * BITS / 8;
+    // the values of unit k (vectors k, k + P, ... of the group), widened
+    auto load_unit = [&](uint32_t k, float (&v)[M][kLaneElems]) {
+#pragma unroll
+        for (int j = 0; j < M; ++j) widen8<DT>(ldv<u32x4, true>(xg, (k + j * m.P) * 16u), v[j]);
+    };
+    auto minmax_unit = [&](const float (&v)[M][kLaneElems], float &mn, float &mx) {
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            float a, b;
+            minmax8(v[j], a, b);
+            mn = __builtin_fminf(mn, a);
+            mx = __builtin_fmaxf(mx, b);
+        }
+    };
+    auto store_unit = [&](uint32_t k, const float (&v)[M][kLaneElems], const GroupParams &p) {
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            uint32_t w[W];
+            encode8<BITS>(v[j], p, w);
+            store_codes<BITS, true>(cg, (k + j * m.P) * kLaneElems, w);
+        }
+    };
     if (!m.wide) {
-        float v[kLaneElems];
+        float v[M][kLaneElems];
         float mn = kInf, mx = -kInf;
         if (sl.active) {
-            widen8<DT>(ldv<u32x4, true>(xg, sl.k * 16u), v);
-            minmax8(v, mn, mx);
+            load_unit(sl.k, v);
+            minmax_unit(v, mn, mx);
         }
         segment_minmax(mn, mx, m.p2_shift);
         const GroupParams p = group_params<BITS>(mn, mx);
         if (!sl.active) return;
-        uint32_t w[W];
-        encode8<BITS>(v, p, w);
-        store_codes<BITS, true>(cg, sl.k * kLaneElems, w);
+        store_unit(sl.k, v, p);
         if (sl.k == 0) {
             s_out[sl.group] = p.s16;
             z_out[sl.group] = p.z16;
@@ -312,20 +348,16 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_oct_kernel(
     }
     float mn = kInf, mx = -kInf;
     for (uint32_t k = sl.k; k < m.P; k += kWave) {
-        float v[kLaneElems], a, b;
-        widen8<DT>(ldv<u32x4, true>(xg, k * 16u), v);
-        minmax8(v, a, b);
-        mn = __builtin_fminf(mn, a);
-        mx = __builtin_fmaxf(mx, b);
+        float v[M][kLaneElems];
+        load_unit(k, v);
+        minmax_unit(v, mn, mx);
     }
     lanes_minmax<kWave>(mn, mx);
     const GroupParams p = group_params<BITS>(mn, mx);
     for (uint32_t k = sl.k; k < m.P; k += kWave) {
-        float v[kLaneElems];
-        widen8<DT>(ldv<u32x4, true>(xg, k * 16u), v);
-        uint32_t w[W];
-        encode8<BITS>(v, p, w);
-        store_codes<BITS, true>(cg, k * kLaneElems, w);
+        float v[M][kLaneElems];
+        load_unit(k, v);
+        store_unit(k, v, p);
     }
     if (sl.k == 0) {
         s_out[sl.group] = p.s16;
@@ -333,52 +365,86 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_oct_kernel(
     }
 }
 
-// binary32 sums of the 8 positions [e, e + 8) over the R operands (ascending r,
-// from operand 0; each term fp32(q*s + z), the product exact); g1 = e / G1,
-// the stage-1 group of the octet (G1 is a multiple of 8, so one group)
+// Operand r's term of the binary32 sums of the 8 positions [e, e + 8):
+// y = x_0 for r = 0, else y + x_r, with x_r = fp32(q*s + z) (the product
+// exact) for the stage-1 scale and zero (s16, z16) of the vector. Called in
+// ascending r, this is the sum in the method's order.
 template <int BITS1>
-__device__ __forceinline__ void sum_oct(const uint8_t *codes1, const uint16_t *s1,
-                                        const uint16_t *z1, int R, uint64_t n, uint64_t per_op,
-                                        uint64_t g1, uint64_t e, float (&y)[kLaneElems]) {
-    for (int r = 0; r < R; ++r) {
-        uint32_t w[BITS1 == 4 ? 1 : 2];
-        load_codes<BITS1, false>(codes1 + ((uint64_t)r * n + e) * BITS1 / 8, 0, w);
-        const uint64_t mi = (uint64_t)r * per_op + g1;
-        float xh[kLaneElems];
-        dequant8<BITS1>(w, s1[mi], z1[mi], xh);
+__device__ __forceinline__ void add_operand(const uint8_t *codes1, int r, uint64_t n, uint64_t e,
+                                            uint16_t s16, uint16_t z16, float (&y)[kLaneElems]) {
+    uint32_t w[BITS1 == 4 ? 1 : 2];
+    load_codes<BITS1, false>(codes1 + ((uint64_t)r * n + e) * BITS1 / 8, 0, w);
+    float xh[kLaneElems];
+    dequant8<BITS1>(w, s16, z16, xh);
 #pragma unroll
-        for (int i = 0; i < kLaneElems; ++i) y[i] = r == 0 ? xh[i] : y[i] + xh[i];
-    }
+    for (int i = 0; i < kLaneElems; ++i) y[i] = r == 0 ? xh[i] : y[i] + xh[i];
 }
 
-template <int BITS1, int BITS2>
+// same_groups: G1 == G2 (the stage-1 group of every position of a stage-2
+// group is then that group)
+template <int BITS1, int BITS2, int M>
 __global__ __launch_bounds__(kBlockThreads) void dsr_oct_kernel(
     const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ s1,
-    const uint16_t *__restrict__ z1, int R, uint64_t n, uint32_t G1, uint32_t G2, PairMap m,
-    uint8_t *__restrict__ codes2, uint16_t *__restrict__ s2, uint16_t *__restrict__ z2) {
+    const uint16_t *__restrict__ z1, int R, uint64_t n, uint64_t per_op, GroupDiv D1,
+    bool same_groups, uint64_t groups, uint32_t G2, PairMap m, uint8_t *__restrict__ codes2,
+    uint16_t *__restrict__ s2, uint16_t *__restrict__ z2) {
     constexpr int W = BITS2 == 4 ? 1 : 2;
-    const uint64_t groups = n / G2;
-    const uint64_t per_op = n / G1;
     Slot sl;
     if (!lane_slot(m, groups, sl)) return;
     const uint64_t base = sl.group * G2;
     uint8_t *cg = codes2 + base * BITS2 / 8;
-    // the stage-1 group of position e: the stage-2 group itself when G1 == G2
-    auto g1_of = [&](uint64_t e) { return G1 == G2 ? sl.group : div_u64(e, G1); };
+    // the sums of unit k, operand by operand (each stage-1 scale and zero
+    // loaded once per operand when the groups coincide)
+    auto sum_unit = [&](uint32_t k, float (&y)[M][kLaneElems]) {
+        auto pos = [&](int j) { return base + (uint64_t)(k + j * m.P) * kLaneElems; };
+        if (same_groups) {
+            for (int r = 0; r < R; ++r) {
+                const uint64_t mi = (uint64_t)r * per_op + sl.group;
+                const uint16_t s16 = s1[mi], z16 = z1[mi];
+#pragma unroll
+                for (int j = 0; j < M; ++j) add_operand<BITS1>(codes1, r, n, pos(j), s16, z16, y[j]);
+            }
+        } else {
+            uint64_t g1[M];
+#pragma unroll
+            for (int j = 0; j < M; ++j) g1[j] = group_of(pos(j), D1);
+            for (int r = 0; r < R; ++r) {
+#pragma unroll
+                for (int j = 0; j < M; ++j) {
+                    const uint64_t mi = (uint64_t)r * per_op + g1[j];
+                    add_operand<BITS1>(codes1, r, n, pos(j), s1[mi], z1[mi], y[j]);
+                }
+            }
+        }
+    };
+    auto minmax_unit = [&](const float (&y)[M][kLaneElems], float &mn, float &mx) {
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            float a, b;
+            minmax8(y[j], a, b);
+            mn = __builtin_fminf(mn, a);
+            mx = __builtin_fmaxf(mx, b);
+        }
+    };
+    auto store_unit = [&](uint32_t k, const float (&y)[M][kLaneElems], const GroupParams &p) {
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            uint32_t w[W];
+            encode8<BITS2>(y[j], p, w);
+            store_codes<BITS2, false>(cg, (k + j * m.P) * kLaneElems, w);
+        }
+    };
     if (!m.wide) {
-        float y[kLaneElems];
+        float y[M][kLaneElems];
         float mn = kInf, mx = -kInf;
         if (sl.active) {
-            const uint64_t e = base + (uint64_t)sl.k * kLaneElems;
-            sum_oct<BITS1>(codes1, s1, z1, R, n, per_op, g1_of(e), e, y);
-            minmax8(y, mn, mx);
+            sum_unit(sl.k, y);
+            minmax_unit(y, mn, mx);
         }
         segment_minmax(mn, mx, m.p2_shift);
         const GroupParams p = group_params<BITS2>(mn, mx);
         if (!sl.active) return;
-        uint32_t w[W];
-        encode8<BITS2>(y, p, w);
-        store_codes<BITS2, false>(cg, sl.k * kLaneElems, w);
+        store_unit(sl.k, y, p);
         if (sl.k == 0) {
             s2[sl.group] = p.s16;
             z2[sl.group] = p.z16;
@@ -387,22 +453,16 @@ __global__ __launch_bounds__(kBlockThreads) void dsr_oct_kernel(
     }
     float mn = kInf, mx = -kInf;
     for (uint32_t k = sl.k; k < m.P; k += kWave) {
-        const uint64_t e = base + (uint64_t)k * kLaneElems;
-        float y[kLaneElems], a, b;
-        sum_oct<BITS1>(codes1, s1, z1, R, n, per_op, g1_of(e), e, y);
-        minmax8(y, a, b);
-        mn = __builtin_fminf(mn, a);
-        mx = __builtin_fmaxf(mx, b);
+        float y[M][kLaneElems];
+        sum_unit(k, y);
+        minmax_unit(y, mn, mx);
     }
     lanes_minmax<kWave>(mn, mx);
     const GroupParams p = group_params<BITS2>(mn, mx);
     for (uint32_t k = sl.k; k < m.P; k += kWave) {
-        const uint64_t e = base + (uint64_t)k * kLaneElems;
-        float y[kLaneElems];
-        sum_oct<BITS1>(codes1, s1, z1, R, n, per_op, g1_of(e), e, y);
-        uint32_t w[W];
-        encode8<BITS2>(y, p, w);
-        store_codes<BITS2, false>(cg, k * kLaneElems, w);
+        float y[M][kLaneElems];
+        sum_unit(k, y);
+        store_unit(k, y, p);
     }
     if (sl.k == 0) {
         s2[sl.group] = p.s16;
@@ -410,16 +470,16 @@ __global__ __launch_bounds__(kBlockThreads) void dsr_oct_kernel(
     }
 }
 
-// one octet of positions per lane
+// one 8-value vector of positions per lane
 template <int DT, int BITS, bool RES>
 __global__ __launch_bounds__(kBlockThreads) void dequant_oct_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ s,
-    const uint16_t *__restrict__ z, uint64_t n, uint32_t G2, const uint16_t *res, uint16_t *out) {
+    const uint16_t *__restrict__ z, uint64_t n, GroupDiv D2, const uint16_t *res, uint16_t *out) {
     const uint64_t e = (wave_index() * kWave + (uint64_t)lane_id()) * kLaneElems;
     if (e >= n) return;
     uint32_t w[BITS == 4 ? 1 : 2];
     load_codes<BITS, false>(codes + e * BITS / 8, 0, w);
-    const uint64_t g = div_u64(e, G2);
+    const uint64_t g = group_of(e, D2);
     float q[kLaneElems], o[kLaneElems];
     decode8<BITS>(w, q);
     const float sf = half_bits_to_float(s[g]);
@@ -438,7 +498,7 @@ __global__ __launch_bounds__(kBlockThreads) void dequant_oct_kernel(
     stv<u32x4, true>(out + e, 0, packed);
 }
 
-// unit: the values a lane takes at a time (2, or 8 for the octet kernels)
+// unit: the values a lane takes at a time
 PairMap pair_map(uint32_t G, uint32_t unit) {
     PairMap m;
     m.P = G / unit;
@@ -446,6 +506,31 @@ PairMap pair_map(uint32_t G, uint32_t unit) {
     m.p2_shift = 0;
     while (!m.wide && (1u << m.p2_shift) < m.P) ++m.p2_shift;
     return m;
+}
+
+// vectors of 8 values per lane unit for a group of G (a multiple of 8)
+// values (measured on groups of 96, 160 and 6144: the single pass with 12
+// vectors per lane beats the two-pass loop over units of 1 or 3 vectors in
+// both kernels)
+int unit_vectors(uint32_t G) {
+    const uint32_t o = G / kLaneElems;
+    uint32_t p = 1;
+    while (p < (uint32_t)kWave && o % (2 * p) == 0) p *= 2;
+    const uint32_t M = o / p;
+    const bool ok = p >= 4 && (M == 3 || M == 5 || M == 6 || M == 7 || M == 10 || M == 12);
+    return ok ? (int)M : 1;
+}
+
+// divisor by d (>= 2) for positions below `n`
+GroupDiv group_div(uint32_t d, uint64_t n) {
+    GroupDiv D;
+    D.d = d;
+    D.wide = n > 0xFFFFFFFFull;
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    D.m = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+    D.l1 = l - 1;
+    return D;
 }
 
 // workgroups for `groups` groups laid out by m
@@ -458,64 +543,127 @@ hipError_t grid_for(const PairMap &m, uint64_t groups, unsigned *blocks) {
     return hipSuccess;
 }
 
+template <int DT, int BITS, int M>
+void go_quantize_oct(unsigned blocks, hipStream_t stream, const uint16_t *x, uint64_t groups,
+                     uint32_t G, const PairMap &m, uint8_t *codes, uint16_t *s, uint16_t *z) {
+    hipLaunchKernelGGL((quantize_oct_kernel<DT, BITS, M>), dim3(blocks), dim3(kBlockThreads), 0,
+                       stream, x, groups, G, m, codes, s, z);
+}
+
+// false for an M without kernels
+template <int DT, int BITS>
+bool go_quantize(int M, unsigned blocks, hipStream_t stream, const uint16_t *x, uint64_t groups,
+                 uint32_t G, const PairMap &m, uint8_t *codes, uint16_t *s, uint16_t *z) {
+    switch (M) {
+    case 0:
+        hipLaunchKernelGGL((quantize_generic_kernel<DT, BITS>), dim3(blocks), dim3(kBlockThreads),
+                           0, stream, x, groups, G, m, codes, s, z);
+        return true;
+#define FC_M(MV)                                                                   \
+    case MV:                                                                       \
+        go_quantize_oct<DT, BITS, MV>(blocks, stream, x, groups, G, m, codes, s, z); \
+        return true
+        FC_M(1);
+        FC_M(3);
+        FC_M(5);
+        FC_M(6);
+        FC_M(7);
+        FC_M(10);
+        FC_M(12);
+#undef FC_M
+    default: return false;
+    }
+}
+
+template <int B1, int B2, int M>
+void go_dsr_oct(unsigned blocks, hipStream_t stream, const uint8_t *codes1, const uint16_t *s1,
+                const uint16_t *z1, int R, uint64_t n, uint64_t per_op, const GroupDiv &D1,
+                bool same, uint64_t groups, uint32_t G2, const PairMap &m, uint8_t *codes2,
+                uint16_t *s2, uint16_t *z2) {
+    hipLaunchKernelGGL((dsr_oct_kernel<B1, B2, M>), dim3(blocks), dim3(kBlockThreads), 0, stream,
+                       codes1, s1, z1, R, n, per_op, D1, same, groups, G2, m, codes2, s2, z2);
+}
+
+// false for an M without kernels
+template <int B1, int B2>
+bool go_dsr(int M, unsigned blocks, hipStream_t stream, const uint8_t *codes1, const uint16_t *s1,
+            const uint16_t *z1, int R, uint64_t n, uint64_t per_op, const GroupDiv &D1, bool same,
+            uint64_t groups, uint32_t G2, const PairMap &m, uint8_t *codes2, uint16_t *s2,
+            uint16_t *z2) {
+    switch (M) {
+    case 0:
+        hipLaunchKernelGGL((dsr_generic_kernel<B1, B2>), dim3(blocks), dim3(kBlockThreads), 0,
+                           stream, codes1, s1, z1, R, n, per_op, D1, groups, G2, m, codes2, s2, z2);
+        return true;
+#define FC_M(MV)                                                                                \
+    case MV:                                                                                    \
+        go_dsr_oct<B1, B2, MV>(blocks, stream, codes1, s1, z1, R, n, per_op, D1, same, groups, G2, \
+                               m, codes2, s2, z2);                                              \
+        return true
+        FC_M(1);
+        FC_M(3);
+        FC_M(5);
+        FC_M(6);
+        FC_M(7);
+        FC_M(10);
+        FC_M(12);
+#undef FC_M
+    default: return false;
+    }
+}
+
+template <int DT, int B, bool RS>
+void go_dequant(bool oct, dim3 grid, hipStream_t stream, const uint8_t *codes2,
+                const uint16_t *s2, const uint16_t *z2, uint64_t n, const GroupDiv &D2,
+                const uint16_t *residual, uint16_t *out) {
+    if (oct)
+        hipLaunchKernelGGL((dequant_oct_kernel<DT, B, RS>), grid, dim3(kBlockThreads), 0, stream,
+                           codes2, s2, z2, n, D2, residual, out);
+    else
+        hipLaunchKernelGGL((dequant_generic_kernel<DT, B, RS>), grid, dim3(kBlockThreads), 0,
+                           stream, codes2, s2, z2, n, D2, residual, out);
+}
+
 }  // namespace
 
+// M = 0 selects the 2-value units
 hipError_t launch_quantize_generic(const uint16_t *x, int dtype, uint64_t n, int bits, int group,
                                    uint8_t *codes, uint16_t *s, uint16_t *z, hipStream_t stream) {
-    const bool oct = group % kLaneElems == 0;
-    const PairMap m = pair_map((uint32_t)group, oct ? kLaneElems : 2);
+    const uint32_t G = (uint32_t)group;
+    const int M = G % kLaneElems == 0 ? unit_vectors(G) : 0;
+    const PairMap m = pair_map(G, M ? M * kLaneElems : 2);
+    const uint64_t groups = n / G;
     unsigned blocks = 0;
-    hipError_t e = grid_for(m, n / (uint64_t)group, &blocks);
+    hipError_t e = grid_for(m, groups, &blocks);
     if (e != hipSuccess) return e;
-#define FC_GO(DT, B)                                                                              \
-    do {                                                                                          \
-        if (oct)                                                                                  \
-            hipLaunchKernelGGL((quantize_oct_kernel<DT, B>), dim3(blocks), dim3(kBlockThreads),   \
-                               0, stream, x, n, (uint32_t)group, m, codes, s, z);                 \
-        else                                                                                      \
-            hipLaunchKernelGGL((quantize_generic_kernel<DT, B>), dim3(blocks),                    \
-                               dim3(kBlockThreads), 0, stream, x, n, (uint32_t)group, m, codes,   \
-                               s, z);                                                             \
-    } while (0)
-    if (dtype == 0) {
-        if (bits == 4) FC_GO(0, 4);
-        else FC_GO(0, 8);
-    } else {
-        if (bits == 4) FC_GO(1, 4);
-        else FC_GO(1, 8);
-    }
-#undef FC_GO
-    return hipGetLastError();
+    const bool ok = dtype == 0
+                        ? (bits == 4 ? go_quantize<0, 4>(M, blocks, stream, x, groups, G, m, codes, s, z)
+                                     : go_quantize<0, 8>(M, blocks, stream, x, groups, G, m, codes, s, z))
+                        : (bits == 4 ? go_quantize<1, 4>(M, blocks, stream, x, groups, G, m, codes, s, z)
+                                     : go_quantize<1, 8>(M, blocks, stream, x, groups, G, m, codes, s, z));
+    return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 
 hipError_t launch_dsr_generic(const uint8_t *codes1, const uint16_t *s1, const uint16_t *z1, int R,
                               uint64_t n, int bits1, int bits2, int group1, int group2,
                               uint8_t *codes2, uint16_t *s2, uint16_t *z2, hipStream_t stream) {
-    const bool oct = group1 % kLaneElems == 0 && group2 % kLaneElems == 0;
-    const PairMap m = pair_map((uint32_t)group2, oct ? kLaneElems : 2);
+    const uint32_t G1 = (uint32_t)group1, G2 = (uint32_t)group2;
+    const bool same = G1 == G2;
+    const int M = G1 % kLaneElems || G2 % kLaneElems ? 0 : unit_vectors(G2);
+    const PairMap m = pair_map(G2, M ? M * kLaneElems : 2);
+    const uint64_t groups = n / G2;
+    const uint64_t per_op = n / G1;
+    const GroupDiv D1 = group_div(G1, n);
     unsigned blocks = 0;
-    hipError_t e = grid_for(m, n / (uint64_t)group2, &blocks);
+    hipError_t e = grid_for(m, groups, &blocks);
     if (e != hipSuccess) return e;
-#define FC_GO(B1, B2)                                                                              \
-    do {                                                                                           \
-        if (oct)                                                                                   \
-            hipLaunchKernelGGL((dsr_oct_kernel<B1, B2>), dim3(blocks), dim3(kBlockThreads), 0,     \
-                               stream, codes1, s1, z1, R, n, (uint32_t)group1, (uint32_t)group2,   \
-                               m, codes2, s2, z2);                                                 \
-        else                                                                                       \
-            hipLaunchKernelGGL((dsr_generic_kernel<B1, B2>), dim3(blocks), dim3(kBlockThreads),    \
-                               0, stream, codes1, s1, z1, R, n, (uint32_t)group1,                  \
-                               (uint32_t)group2, m, codes2, s2, z2);                               \
-    } while (0)
-    if (bits1 == 4) {
-        if (bits2 == 4) FC_GO(4, 4);
-        else FC_GO(4, 8);
-    } else {
-        if (bits2 == 4) FC_GO(8, 4);
-        else FC_GO(8, 8);
-    }
+#define FC_GO(B1, B2)                                                                             \
+    go_dsr<B1, B2>(M, blocks, stream, codes1, s1, z1, R, n, per_op, D1, same, groups, G2, m, codes2, \
+                   s2, z2)
+    const bool ok = bits1 == 4 ? (bits2 == 4 ? FC_GO(4, 4) : FC_GO(4, 8))
+                               : (bits2 == 4 ? FC_GO(8, 4) : FC_GO(8, 8));
 #undef FC_GO
-    return hipGetLastError();
+    return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 
 hipError_t launch_dequantize_generic(const uint8_t *codes2, const uint16_t *s2, const uint16_t *z2,
@@ -526,15 +674,8 @@ hipError_t launch_dequantize_generic(const uint8_t *codes2, const uint16_t *s2, 
     const uint64_t b = (lanes + kBlockThreads - 1) / kBlockThreads;
     if (b > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)b);
-#define FC_GO(DT, B, RS)                                                                      \
-    do {                                                                                      \
-        if (oct)                                                                              \
-            hipLaunchKernelGGL((dequant_oct_kernel<DT, B, RS>), grid, dim3(kBlockThreads), 0, \
-                               stream, codes2, s2, z2, n, (uint32_t)group2, residual, out);   \
-        else                                                                                  \
-            hipLaunchKernelGGL((dequant_generic_kernel<DT, B, RS>), grid, dim3(kBlockThreads), \
-                               0, stream, codes2, s2, z2, n, (uint32_t)group2, residual, out); \
-    } while (0)
+    const GroupDiv D2 = group_div((uint32_t)group2, n);
+#define FC_GO(DT, B, RS) go_dequant<DT, B, RS>(oct, grid, stream, codes2, s2, z2, n, D2, residual, out)
     const bool res = residual != nullptr;
     if (dtype == 0) {
         if (bits == 4) { if (res) FC_GO(0, 4, true); else FC_GO(0, 4, false); }

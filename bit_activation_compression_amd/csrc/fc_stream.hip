@@ -8,11 +8,16 @@
 //   kind 1  read 4, write 1 read n bytes, write n/4 bytes (the stage-1
 //                           quantizer's shape: 16-bit values in, 4-bit codes out)
 //   kind 2  read            read n bytes (one 4-byte word written per wave)
+//   kind 3  read 1, write 4 read n bytes, write 4n bytes (the final
+//                           dequantizer's shape: 4-bit codes in, 16-bit values
+//                           out)
 //
-// Same access pattern as the quantizer: a wave owns a tile of U slots, a slot
-// is 64 lanes x 16 bytes read (non-temporal), and the written part of a slot
-// is one contiguous run per wave (non-temporal). The loaded data feeds what
-// is written (an xor of the lane's words), so no load can be dropped.
+// Kinds 0 to 2 follow the quantizer's access pattern: a wave owns a tile of U
+// slots, a slot is 64 lanes x 16 bytes read (non-temporal), and the written
+// part of a slot is one contiguous run per wave (non-temporal). Kind 3
+// follows the dequantizer's: a slot is 64 lanes x 4 bytes read (cached) and
+// 64 lanes x 16 bytes written (non-temporal). The loaded data feeds what is
+// written, so no load can be dropped.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -63,8 +68,43 @@ __global__ __launch_bounds__(kBlockThreads) void stream_kernel(const uint8_t *__
     }
 }
 
+// read 1, write 4: lane words of 4 bytes in, 16 bytes out
+template <int U>
+__global__ __launch_bounds__(kBlockThreads) void expand_kernel(const uint8_t *__restrict__ src,
+                                                               uint8_t *__restrict__ dst,
+                                                               uint64_t n) {
+    constexpr uint32_t kSlot = kWave * 4;   // bytes read per slot
+    const int lane = lane_id();
+    const uint64_t tile = wave_index() * (uint64_t)(U * kSlot);
+    if (tile >= n) return;
+    const uint64_t left = n - tile;
+    const uint32_t avail = left < (uint64_t)(U * kSlot) ? (uint32_t)left : U * kSlot;
+    const uint8_t *sb = src + tile;
+    uint8_t *db = dst + 4 * tile;
+    uint32_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t rel = u * kSlot + lane * 4u;
+        v[u] = ldv<uint32_t, false>(sb, rel < avail ? rel : 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t rel = u * kSlot + lane * 4u;
+        const u32x4 w = {v[u], v[u] ^ 1u, v[u] ^ 2u, v[u] ^ 3u};
+        if (rel < avail) stv<u32x4, true>(db, rel * 4u, w);
+    }
+}
+
 template <int KIND, int U>
 hipError_t launch(const void *src, void *dst, uint64_t n, hipStream_t stream) {
+    if constexpr (KIND == 3) {
+        constexpr uint64_t per_block = (uint64_t)kWavesPerBlock * U * kWave * 4;
+        const uint64_t blocks = (n + per_block - 1) / per_block;
+        if (blocks > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((expand_kernel<U>), dim3((unsigned)blocks), dim3(kBlockThreads), 0,
+                           stream, static_cast<const uint8_t *>(src), static_cast<uint8_t *>(dst), n);
+        return hipGetLastError();
+    }
     constexpr uint64_t per_block = (uint64_t)kWavesPerBlock * U * kWave * 16;
     const uint64_t blocks = (n + per_block - 1) / per_block;
     if (blocks > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
@@ -115,13 +155,14 @@ extern "C" int fc_internal_clock_probe(void *out, int iters, void *stream) {
 
 extern "C" int fc_internal_stream_probe(int kind, int slots, const void *src, void *dst,
                                         size_t bytes, void *stream) {
-    if (kind < 0 || kind > 2 || (slots != 1 && slots != 2 && slots != 4 && slots != 8)) return 2;
+    if (kind < 0 || kind > 3 || (slots != 1 && slots != 2 && slots != 4 && slots != 8)) return 2;
     if (bytes == 0) return 0;
     if (src == nullptr || dst == nullptr) return 1;
     if (bytes % 16 != 0 || ((uintptr_t)src & 15u) || ((uintptr_t)dst & 15u)) return 4;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = kind == 0   ? fc::launch_u<0>(slots, src, dst, bytes, s)
                    : kind == 1 ? fc::launch_u<1>(slots, src, dst, bytes, s)
-                               : fc::launch_u<2>(slots, src, dst, bytes, s);
+                   : kind == 2 ? fc::launch_u<2>(slots, src, dst, bytes, s)
+                               : fc::launch_u<3>(slots, src, dst, bytes, s);
     return e == hipSuccess ? 0 : 6;
 }

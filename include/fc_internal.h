@@ -22,6 +22,8 @@ extern "C" {
  *           4-byte word per 16 bytes read: the xor of its four words)
  *   kind 2  read:             reads src, writes one 4-byte word per wave
  *           tile (dst must hold 4 * ceil(bytes / (slots * 1024)) bytes)
+ *   kind 3  read 1, write 4:  reads src, writes 4 * bytes bytes of dst (16
+ *           bytes per 4 read)
  * slots: 16-byte loads each lane keeps in flight (1, 2, 4 or 8).
  * Returns 0, or 1 (NULL pointer), 2 (bad kind or slots), 4 (alignment or
  * size not a multiple of 16), 6 (launch error). bytes == 0 enqueues nothing.

@@ -209,7 +209,10 @@ def test_stream_probe_validates():
     P = L.fc_internal_stream_probe
     P.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                   ctypes.c_void_p]
-    assert P(3, 4, FAKE, FAKE, 1024, None) == 2
+    assert P(4, 4, FAKE, FAKE, 1024, None) == 2
+    assert P(-1, 4, FAKE, FAKE, 1024, None) == 2
+    assert P(3, 5, FAKE, FAKE, 1024, None) == 2
+    assert P(3, 4, FAKE, MISALIGNED, 1024, None) == 4
     assert P(0, 3, FAKE, FAKE, 1024, None) == 2
     assert P(0, 16, FAKE, FAKE, 1024, None) == 2
     assert P(0, 4, None, FAKE, 1024, None) == 1

@@ -102,6 +102,11 @@ CASES = [  # R, T, H, bits1, bits2, group, dtype
     (4, 3, 48, 8, 4, 16, synth.BF16),        # stage 1 fast (16), stage 2 (12) in pairs
     (3, 4, 24, 4, 8, 12, synth.F16),         # stage 1 in pairs, stage 2 fast (8)
     (2, 7, 1040, 8, 8, 520, synth.BF16),     # 65 octets: one group per wave
+    (4, 6, 448, 4, 4, 56, synth.F16),        # units of 7 vectors, one lane per group
+    (2, 5, 2240, 8, 4, 224, synth.BF16),     # units of 7 vectors, 4 lanes per group
+    (2, 3, 10240, 4, 4, 5120, synth.F16),    # units of 5 vectors, one group per wave
+    (1, 2, 7168, 8, 8, 7168, synth.BF16),    # units of 7 vectors, one group per wave
+    (4, 9, 2560, 4, 4, 160, synth.BF16),     # units of 5 vectors, 4 lanes per group
 ]
 
 
