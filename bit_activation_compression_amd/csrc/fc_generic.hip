@@ -297,7 +297,11 @@ __global__ __launch_bounds__(kBlockThreads) void dequant_generic_kernel(
 // 8-value vectors (see the top of the file); a PairMap whose P counts units
 // ---------------------------------------------------------------------------
 
-template <int DT, int BITS, int M>
+// NT: non-temporal loads, for groups of 64 or more lanes (each load
+// instruction then reads whole lines); shorter segments read 64-byte pieces
+// of lines whose other halves the next instruction reads, which the cached
+// loads serve from L1
+template <int DT, int BITS, int M, bool NT>
 __global__ __launch_bounds__(kBlockThreads) void quantize_oct_kernel(
     const uint16_t *__restrict__ x, uint64_t groups, uint32_t G, PairMap m,
     uint8_t *__restrict__ codes, uint16_t *__restrict__ s_out, uint16_t *__restrict__ z_out) {
@@ -310,7 +314,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_oct_kernel(
     // the values of unit k (vectors k, k + P, ... of the group), widened
     auto load_unit = [&](uint32_t k, float (&v)[M][kLaneElems]) {
 #pragma unroll
-        for (int j = 0; j < M; ++j) widen8<DT>(ldv<u32x4, true>(xg, (k + j * m.P) * 16u), v[j]);
+        for (int j = 0; j < M; ++j) widen8<DT>(ldv<u32x4, NT>(xg, (k + j * m.P) * 16u), v[j]);
     };
     auto minmax_unit = [&](const float (&v)[M][kLaneElems], float &mn, float &mx) {
 #pragma unroll
@@ -546,8 +550,12 @@ hipError_t grid_for(const PairMap &m, uint64_t groups, unsigned *blocks) {
 template <int DT, int BITS, int M>
 void go_quantize_oct(unsigned blocks, hipStream_t stream, const uint16_t *x, uint64_t groups,
                      uint32_t G, const PairMap &m, uint8_t *codes, uint16_t *s, uint16_t *z) {
-    hipLaunchKernelGGL((quantize_oct_kernel<DT, BITS, M>), dim3(blocks), dim3(kBlockThreads), 0,
-                       stream, x, groups, G, m, codes, s, z);
+    if (m.wide || m.P == (uint32_t)kWave)
+        hipLaunchKernelGGL((quantize_oct_kernel<DT, BITS, M, true>), dim3(blocks),
+                           dim3(kBlockThreads), 0, stream, x, groups, G, m, codes, s, z);
+    else
+        hipLaunchKernelGGL((quantize_oct_kernel<DT, BITS, M, false>), dim3(blocks),
+                           dim3(kBlockThreads), 0, stream, x, groups, G, m, codes, s, z);
 }
 
 // false for an M without kernels
