@@ -64,6 +64,10 @@ PEAK_VALU_G_WAVE_INSTR = 256 * 4 * 2.4 / 4
 BREAKDOWN_STEPS = 50   # steps of the per-kernel event pass
 GRAPH_CALLS = 20       # calls captured per HIP graph in the launch-bound measurements
 LINEAR_ROUNDS = 3      # interleaved timing rounds of the linear-layer variants
+SWEEP_SETS = 4         # operand copies of the sweep (134 MB each) read in turn
+GENERIC_SETS = 3       # and of the generic-group shape (168 MB each)
+EVICT_BYTES = 1 << 30  # scratch written before each cache-cold call (L2s and the 256 MB Infinity Cache)
+COLD_CALLS = 30        # cache-cold calls timed one by one
 CPU_PASSES = 3         # passes of the CPU oracle over the whole workload (~4-5 s each)
 SETTLE_MIN_MS = 60.0   # least back-to-back time before the clock is taken as steady
 SETTLE_MAX_MS = 800.0
@@ -249,6 +253,21 @@ def timed_calls(torch, fn, stream, n) -> float:
     return e[0].elapsed_time(e[1]) / n
 
 
+def cold_us_per_call(torch, fn, stream, scratch, n: int = COLD_CALLS) -> float:
+    """Median microseconds of n calls, each timed on its own with HIP events right after a
+    1 GiB scratch write on the same stream (outside the events), so that neither the L2s nor
+    the Infinity Cache hold the call's inputs or payloads."""
+    ev = _events(torch, 2 * n)
+    for i in range(n):
+        scratch.fill_(i & 0xFF)
+        ev[2 * i].record(stream)
+        fn()
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    us = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(n))
+    return us[n // 2]
+
+
 def stage_errors(torch, fc, xf, out, ws, R, T, H, bits, bits2, g, g2) -> dict:
     """Per-element MSE of each stage, from the payloads the library wrote (torch on the GPU):
       stage1_mse: mean over r, t, h of (dequantized payload 1 - x)^2
@@ -379,47 +398,57 @@ def other_workloads(torch, np, fc, synth, seed, dev, stream) -> dict:
     del xs, bufs
     torch.cuda.empty_cache()
 
-    # the group-size sweep: one set of operands for every width and group length
+    # the group-size sweep: the same operands for every width and group length, in
+    # SWEEP_SETS copies (with their own payloads and outputs) read in turn, so that a step
+    # does not find its inputs in the Infinity Cache
     base = synth.workload("sweep_int4_g128")
     tdt = torch.float16 if base.dtype == synth.F16 else torch.bfloat16
     xh = synth.operands(base, seed)
-    xd = put(xh, tdt)
+    xds = [put(xh, tdt) for _ in range(SWEEP_SETS)]
     del xh
-    xf = xd.float()
+    xf = xds[0].float()
     sweep = []
     for bits in synth.SWEEP_BITS:
         for g in synth.SWEEP_GROUPS:
             R, T, H = base.R, base.T, base.H
             g2 = fc.fc_stage2_group(R, H, g)
-            out, ws = fc.fc_allreduce_emulated(xd, bits, g)
+            bufs = [fc.fc_allreduce_emulated(x, bits, g) for x in xds]
             rec = {"bits": bits, "group": g, "group2": g2}
-            rec.update(stage_errors(torch, fc, xf, out, ws, R, T, H, bits, bits, g, g2))
+            rec.update(stage_errors(torch, fc, xf, bufs[0][0], bufs[0][1], R, T, H, bits, bits, g, g2))
+            it = [0]
 
-            def calls(bits=bits, g=g, out=out, ws=ws):
-                fc.fc_allreduce_emulated(xd, bits, g, out, ws, stream=stream)
+            def calls(bits=bits, g=g, bufs=bufs):
+                i = it[0] = (it[0] + 1) % SWEEP_SETS
+                fc.fc_allreduce_emulated(xds[i], bits, g, bufs[i][0], bufs[i][1], stream=stream)
 
             settle_clock(torch, calls, stream, min_ms=30.0)
-            ms = timed_calls(torch, calls, stream, 50)
+            ms = timed_calls(torch, calls, stream, 48)
             mb = model_bytes(R, T, H, bits, g, g2)["total"]
             rec.update({"us_per_step": round(ms * 1e3, 2), "gbps": round(mb / (ms * 1e-3) / 1e9, 1)})
             sweep.append(rec)
-            del out, ws
+            del bufs
+    in_mb = base.R * base.T * base.H * 2 / 1e6
     res["sweep"] = {"R": base.R, "T": base.T, "H": base.H, "io_dtype": base.dtype,
-                    "note": "one input set; the same inputs read by every step (cache-warm)",
+                    "note": f"{SWEEP_SETS} copies of the operands ({in_mb:.0f} MB each) with their "
+                            f"own payloads, read in turn",
                     "points": sweep}
-    del xd, xf
+    del xds, xf
     torch.cuda.empty_cache()
 
     # the generic kernels: a hidden size of 5120 (not a power of two; LLaMA-2-13B's) and
     # groups of 160, which the power-of-two kernels do not take
     w = synth.workload("llama3_8b_prefill").with_(T=4096, H=5120, group=160, name="generic_h5120_g160")
     tdt = torch.float16 if w.dtype == synth.F16 else torch.bfloat16
-    xd = put(synth.operands(w, seed), tdt)
-    out, ws = fc.fc_allreduce_emulated(xd, w.bits, w.group)
+    xh = synth.operands(w, seed)
+    xds = [put(xh, tdt) for _ in range(GENERIC_SETS)]
+    del xh
+    bufs = [fc.fc_allreduce_emulated(x, w.bits, w.group) for x in xds]
     g2 = fc.fc_stage2_group(w.R, w.H, w.group)
+    itg = [0]
 
     def callg():
-        fc.fc_allreduce_emulated(xd, w.bits, w.group, out, ws, stream=stream)
+        i = itg[0] = (itg[0] + 1) % GENERIC_SETS
+        fc.fc_allreduce_emulated(xds[i], w.bits, w.group, bufs[i][0], bufs[i][1], stream=stream)
 
     settle_clock(torch, callg, stream, min_ms=30.0)
     ms = timed_calls(torch, callg, stream, 20)
@@ -427,11 +456,15 @@ def other_workloads(torch, np, fc, synth, seed, dev, stream) -> dict:
     res["generic_group"] = {"R": w.R, "T": w.T, "H": w.H, "io_dtype": w.dtype, "bits": w.bits,
                             "group": w.group, "group2": g2, "us_per_step": round(ms * 1e3, 2),
                             "gbps": round(mb / (ms * 1e-3) / 1e9, 1),
-                            "note": "generic kernels (group not a power of two); same inputs "
-                                    "every step"}
-    del xd, out, ws
+                            "note": f"generic kernels (group not a power of two); "
+                                    f"{GENERIC_SETS} copies of the operands read in turn"}
+    del xds, bufs
+    torch.cuda.empty_cache()
 
-    # launch-bound shapes: decode and tiny
+    # launch-bound shapes: decode and tiny; cache-cold calls after a scratch write, and
+    # back-to-back calls (the inputs then stay in the caches, as when the producing layer
+    # has just written them)
+    scratch = torch.empty(EVICT_BYTES, dtype=torch.uint8, device=dev)
     for name in ("decode", "tiny"):
         w = synth.workload(name)
         tdt = torch.float16 if w.dtype == synth.F16 else torch.bfloat16
@@ -460,6 +493,7 @@ def other_workloads(torch, np, fc, synth, seed, dev, stream) -> dict:
         settle_clock(torch, three, stream, min_ms=30.0)
         us_three = timed_calls(torch, three, stream, 200) * 1e3
         us_graph = graph_us_per_call(torch, single, stream, dev)
+        us_cold = cold_us_per_call(torch, single, stream, scratch)
         mb = model_bytes(w.R, w.T, w.H, w.bits, w.group, g2)["total"]
         res[name] = {"R": w.R, "T": w.T, "H": w.H, "io_dtype": w.dtype, "bits": w.bits,
                      "group": w.group, "model_bytes": mb,
@@ -468,11 +502,16 @@ def other_workloads(torch, np, fc, synth, seed, dev, stream) -> dict:
                      "us_per_call_three_launches": round(us_three, 2),
                      "us_per_call_noalloc": round(us_noalloc, 2),
                      "us_per_call_noalloc_in_graph": round(us_noalloc_graph, 2),
+                     "us_per_call_cache_cold": round(us_cold, 2),
                      "gbps_single_launch": round(mb / (us_single * 1e-6) / 1e9, 1),
                      "graph_calls_per_replay": GRAPH_CALLS,
                      "timing": "HIP events around 200 back-to-back calls through the Python "
-                               "binding (launch cost included), after a settle run"}
+                               "binding (launch cost included), after a settle run; cache_cold: "
+                               f"median of {COLD_CALLS} single launches, each timed on its own "
+                               f"after a {EVICT_BYTES >> 20} MiB scratch write"}
         del xd, out, ws, v
+    del scratch
+    torch.cuda.empty_cache()
     return res
 
 
