@@ -1,7 +1,7 @@
 // Reduce-Scatter reduction and requantization before the All-Gather of
 // "Flash Communication: Reducing Tensor Parallelization Bottleneck for Fast
-// Large Language Model Inference" (Figure 5, right; TL;DR "two-step
-// All-Reduce").
+// Large Language Model Inference" (Figure 5, right; the TL;DR's all-reduce
+// in two steps).
 //
 // Chunk j of the hidden dimension (columns [j*C, (j+1)*C), C = H/R) is what
 // rank j reduces. Stage-2 groups of g2 = min(group, C) columns never cross a

@@ -88,7 +88,7 @@ fc_status fc_quantize_groups(const void *x, fc_dtype dt, int R, int T, int H, in
 
 /*
  * The Reduce-Scatter reduction and the quantization before the All-Gather
- * (Figure 5, right; TL;DR "two-step All-Reduce").
+ * (Figure 5, right; TL;DR: the all-reduce in two steps).
  *   codes1, s1, z1  as produced by fc_quantize_groups
  *   codes2 [T][H*bits/8], s2, z2 [T][H/g2] with g2 = fc_stage2_group(R, H, group)
  * For each chunk j, token t and column h of the chunk, the R operands are
@@ -110,8 +110,8 @@ fc_status fc_dequantize(const uint8_t *codes2, const uint16_t *s2, const uint16_
                         int T, int H, int bits, int group2, fc_dtype dt, void *out, void *stream);
 
 /*
- * The whole emulated all-reduce on one GPU (TL;DR: the "two-step All-Reduce"
- * that replaces a ring; Figure 5, right: quantize, Reduce-Scatter, quantize,
+ * The whole emulated all-reduce on one GPU (TL;DR: the all-reduce in two
+ * steps that replaces a ring; Figure 5, right: quantize, Reduce-Scatter, quantize,
  * All-Gather, dequantize): fc_quantize_groups, then fc_dequant_sum_requant,
  * then fc_dequantize, with both payloads placed in the caller's workspace
  * (layout: fc_workspace_layout). out [T][H] in dt.
