@@ -107,6 +107,9 @@ CASES = [  # R, T, H, bits1, bits2, group, dtype
     (2, 3, 10240, 4, 4, 5120, synth.F16),    # units of 5 vectors, one group per wave
     (1, 2, 7168, 8, 8, 7168, synth.BF16),    # units of 7 vectors, one group per wave
     (4, 9, 2560, 4, 4, 160, synth.BF16),     # units of 5 vectors, 4 lanes per group
+    (16, 4, 1536, 4, 4, 96, synth.F16),      # R = 16: the reduction's run-time operand loop
+    (24, 3, 2304, 8, 4, 96, synth.BF16),     # R = 24, mixed widths
+    (12, 5, 1440, 4, 4, 120, synth.F16),     # R = 12, units of 1 vector (15 of 16 lanes)
 ]
 
 

@@ -191,6 +191,29 @@ def test_ragged_shapes(R, T, H, bits, group, dtype):
     _check(_run_steps(x, w), ref, w, x)
 
 
+# more operands than the compile-time reduction paths (2, 4, 8) and the
+# single-launch path (up to 8) take: the reduction's run-time operand loop
+MANY = [
+    # R, T, H, bits, group, dtype
+    (12, 5, 1536, 8, 64, synth.F16),
+    (16, 7, 2048, 4, 128, synth.BF16),
+    (32, 3, 4096, 4, 128, synth.F16),
+    (64, 2, 8192, 8, 128, synth.BF16),
+    (16, 3, 512, 4, 32, synth.F16),
+]
+
+
+@pytest.mark.parametrize("R,T,H,bits,group,dtype", MANY)
+def test_many_operands(R, T, H, bits, group, dtype):
+    w = synth.workload("tiny").with_(name="many", R=R, T=T, H=H, bits=bits, group=group,
+                                     dtype=dtype, outlier_frac=0.01, outlier_scale=20.0)
+    x = synth.operands(w, 11)
+    ref = oracle.allreduce(x, w.dtype, w.bits, w.group, want_f32=False)
+    _say(f"many operands R={R} T={T} H={H} bits={bits} group={group} {dtype}")
+    _check(_run_fused(x, w), ref, w, x)
+    _check(_run_steps(x, w), ref, w, x)
+
+
 def test_empty_token_dimension():
     x = torch.empty((4, 0, 512), dtype=torch.float16, device="cuda")
     out, ws = fc.fc_allreduce_emulated(x, 4, 128)
