@@ -5,17 +5,18 @@
 // Large Language Model Inference" (Figure 5, right; groups along the hidden
 // dimension as in Figure 4), hence the same bits; the layout is simpler.
 //
-// Work layout: a group of G values is P units of a lane. When G is a
-// multiple of 8 (for the reduction step: both group lengths), a unit is M
-// 8-value vectors (16 bytes of 16-bit values each, the fast kernels' per-lane
-// code paths), interleaved over the group's lanes: lane k of P takes vectors
+// Work layout: a group of G values is P lane units. When G is a multiple of
+// 8 (for the reduction step: both group lengths), a unit is M 8-value
+// vectors (16 bytes of 16-bit values each, the fast kernels' per-lane code
+// paths), interleaved over the group's lanes: lane k of the P takes vectors
 // k, k + P, ..., k + (M-1) P, so that each load instruction reads runs of
-// 16 P contiguous bytes. M is G/8P with P the largest power of two dividing
-// G/8, at most 64, when that M is 3, 5, 6, 7, 10 or 12 and P >= 4 (groups of
-// 96, 160, 192, 224, 1536, 5120, 6144 ...), else M = 1. Other groups take
-// units of 2 consecutive values. G is even and groups start at multiples of
-// G, so a unit never straddles two groups, and a 4-bit code pair is one
-// byte. A lane handles units:
+// 16 P contiguous bytes. With p the largest power of two dividing G/8 (at
+// most 64), M = G/8p and P = p when that M is 3, 5, 6, 7, 10 or 12 and
+// p >= 4 (groups of 96, 160, 192, 224, 1536, 5120, 6144 ...); otherwise
+// M = 1 and P = G/8. Other groups take units of 2 consecutive values
+// (P = G/2). G is even and groups start at multiples of G, so a unit never
+// straddles two groups, and a 4-bit code pair is one byte. A lane handles
+// units:
 //   - P <= 64: each group takes an aligned segment of P2 lanes (P2 the next
 //     power of two >= P), 64/P2 groups per wave; lanes k >= P of a segment
 //     are idle. The group's min/max is reduced over its segment with xor
@@ -32,7 +33,7 @@ namespace {
 
 constexpr float kInf = __builtin_inff();
 
-struct PairMap {
+struct UnitMap {
     uint32_t P;          // lane units per group
     uint32_t p2_shift;   // log2 of the lanes per group segment (P <= 64)
     bool wide;           // P > 64: one group per wave
@@ -101,15 +102,15 @@ __device__ __forceinline__ void load_pair_codes(const uint8_t *codes, uint64_t e
     }
 }
 
-// Which group and pair this lane handles (P <= 64), or the group of the wave
-// (P > 64). Returns false for a wave wholly past the last group.
+// Which group and unit this lane handles (P <= 64), or the group of the
+// wave (P > 64). Returns false for a wave wholly past the last group.
 struct Slot {
     uint64_t group;
-    uint32_t k;        // pair index inside the group (first pair when wide)
-    bool active;       // this lane's pair exists (narrow layout)
+    uint32_t k;        // unit index inside the group (the first one when wide)
+    bool active;       // this lane's unit exists (narrow layout)
 };
 
-__device__ __forceinline__ bool lane_slot(const PairMap &m, uint64_t groups, Slot &s) {
+__device__ __forceinline__ bool lane_slot(const UnitMap &m, uint64_t groups, Slot &s) {
     const uint64_t wave = wave_index();
     const uint32_t lane = (uint32_t)lane_id();
     if (m.wide) {
@@ -151,7 +152,7 @@ __device__ __forceinline__ uint64_t group_of(uint64_t e, const GroupDiv &D) {
 // ---------------------------------------------------------------------------
 template <int DT, int BITS>
 __global__ __launch_bounds__(kBlockThreads) void quantize_generic_kernel(
-    const uint16_t *__restrict__ x, uint64_t groups, uint32_t G, PairMap m,
+    const uint16_t *__restrict__ x, uint64_t groups, uint32_t G, UnitMap m,
     uint8_t *__restrict__ codes, uint16_t *__restrict__ s_out, uint16_t *__restrict__ z_out) {
     Slot sl;
     if (!lane_slot(m, groups, sl)) return;
@@ -224,7 +225,7 @@ template <int BITS1, int BITS2>
 __global__ __launch_bounds__(kBlockThreads) void dsr_generic_kernel(
     const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ s1,
     const uint16_t *__restrict__ z1, int R, uint64_t n, uint64_t per_op, GroupDiv D1,
-    uint64_t groups, uint32_t G2, PairMap m, uint8_t *__restrict__ codes2,
+    uint64_t groups, uint32_t G2, UnitMap m, uint8_t *__restrict__ codes2,
     uint16_t *__restrict__ s2, uint16_t *__restrict__ z2) {
     Slot sl;
     if (!lane_slot(m, groups, sl)) return;
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(kBlockThreads) void dequant_generic_kernel(
 
 // ---------------------------------------------------------------------------
 // groups whose length is a multiple of 8: a lane unit is M consecutive
-// 8-value vectors (see the top of the file); a PairMap whose P counts units
+// 8-value vectors (see the top of the file); a UnitMap whose P counts units
 // ---------------------------------------------------------------------------
 
 // NT: non-temporal loads, for groups of 64 or more lanes (each load
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(kBlockThreads) void dequant_generic_kernel(
 // loads serve from L1
 template <int DT, int BITS, int M, bool NT>
 __global__ __launch_bounds__(kBlockThreads) void quantize_oct_kernel(
-    const uint16_t *__restrict__ x, uint64_t groups, uint32_t G, PairMap m,
+    const uint16_t *__restrict__ x, uint64_t groups, uint32_t G, UnitMap m,
     uint8_t *__restrict__ codes, uint16_t *__restrict__ s_out, uint16_t *__restrict__ z_out) {
     constexpr int W = BITS == 4 ? 1 : 2;
     Slot sl;
@@ -390,7 +391,7 @@ template <int BITS1, int BITS2, int M>
 __global__ __launch_bounds__(kBlockThreads) void dsr_oct_kernel(
     const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ s1,
     const uint16_t *__restrict__ z1, int R, uint64_t n, uint64_t per_op, GroupDiv D1,
-    bool same_groups, uint64_t groups, uint32_t G2, PairMap m, uint8_t *__restrict__ codes2,
+    bool same_groups, uint64_t groups, uint32_t G2, UnitMap m, uint8_t *__restrict__ codes2,
     uint16_t *__restrict__ s2, uint16_t *__restrict__ z2) {
     constexpr int W = BITS2 == 4 ? 1 : 2;
     Slot sl;
@@ -503,8 +504,8 @@ __global__ __launch_bounds__(kBlockThreads) void dequant_oct_kernel(
 }
 
 // unit: the values a lane takes at a time
-PairMap pair_map(uint32_t G, uint32_t unit) {
-    PairMap m;
+UnitMap unit_map(uint32_t G, uint32_t unit) {
+    UnitMap m;
     m.P = G / unit;
     m.wide = m.P > (uint32_t)kWave;
     m.p2_shift = 0;
@@ -538,7 +539,7 @@ GroupDiv group_div(uint32_t d, uint64_t n) {
 }
 
 // workgroups for `groups` groups laid out by m
-hipError_t grid_for(const PairMap &m, uint64_t groups, unsigned *blocks) {
+hipError_t grid_for(const UnitMap &m, uint64_t groups, unsigned *blocks) {
     const uint64_t per_wave = m.wide ? 1 : (kWave >> m.p2_shift);
     const uint64_t waves = (groups + per_wave - 1) / per_wave;
     const uint64_t b = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -549,7 +550,7 @@ hipError_t grid_for(const PairMap &m, uint64_t groups, unsigned *blocks) {
 
 template <int DT, int BITS, int M>
 void go_quantize_oct(unsigned blocks, hipStream_t stream, const uint16_t *x, uint64_t groups,
-                     uint32_t G, const PairMap &m, uint8_t *codes, uint16_t *s, uint16_t *z) {
+                     uint32_t G, const UnitMap &m, uint8_t *codes, uint16_t *s, uint16_t *z) {
     if (m.wide || m.P == (uint32_t)kWave)
         hipLaunchKernelGGL((quantize_oct_kernel<DT, BITS, M, true>), dim3(blocks),
                            dim3(kBlockThreads), 0, stream, x, groups, G, m, codes, s, z);
@@ -561,7 +562,7 @@ void go_quantize_oct(unsigned blocks, hipStream_t stream, const uint16_t *x, uin
 // false for an M without kernels
 template <int DT, int BITS>
 bool go_quantize(int M, unsigned blocks, hipStream_t stream, const uint16_t *x, uint64_t groups,
-                 uint32_t G, const PairMap &m, uint8_t *codes, uint16_t *s, uint16_t *z) {
+                 uint32_t G, const UnitMap &m, uint8_t *codes, uint16_t *s, uint16_t *z) {
     switch (M) {
     case 0:
         hipLaunchKernelGGL((quantize_generic_kernel<DT, BITS>), dim3(blocks), dim3(kBlockThreads),
@@ -586,7 +587,7 @@ bool go_quantize(int M, unsigned blocks, hipStream_t stream, const uint16_t *x, 
 template <int B1, int B2, int M>
 void go_dsr_oct(unsigned blocks, hipStream_t stream, const uint8_t *codes1, const uint16_t *s1,
                 const uint16_t *z1, int R, uint64_t n, uint64_t per_op, const GroupDiv &D1,
-                bool same, uint64_t groups, uint32_t G2, const PairMap &m, uint8_t *codes2,
+                bool same, uint64_t groups, uint32_t G2, const UnitMap &m, uint8_t *codes2,
                 uint16_t *s2, uint16_t *z2) {
     hipLaunchKernelGGL((dsr_oct_kernel<B1, B2, M>), dim3(blocks), dim3(kBlockThreads), 0, stream,
                        codes1, s1, z1, R, n, per_op, D1, same, groups, G2, m, codes2, s2, z2);
@@ -596,7 +597,7 @@ void go_dsr_oct(unsigned blocks, hipStream_t stream, const uint8_t *codes1, cons
 template <int B1, int B2>
 bool go_dsr(int M, unsigned blocks, hipStream_t stream, const uint8_t *codes1, const uint16_t *s1,
             const uint16_t *z1, int R, uint64_t n, uint64_t per_op, const GroupDiv &D1, bool same,
-            uint64_t groups, uint32_t G2, const PairMap &m, uint8_t *codes2, uint16_t *s2,
+            uint64_t groups, uint32_t G2, const UnitMap &m, uint8_t *codes2, uint16_t *s2,
             uint16_t *z2) {
     switch (M) {
     case 0:
@@ -639,7 +640,7 @@ hipError_t launch_quantize_generic(const uint16_t *x, int dtype, uint64_t n, int
                                    uint8_t *codes, uint16_t *s, uint16_t *z, hipStream_t stream) {
     const uint32_t G = (uint32_t)group;
     const int M = G % kLaneElems == 0 ? unit_vectors(G) : 0;
-    const PairMap m = pair_map(G, M ? M * kLaneElems : 2);
+    const UnitMap m = unit_map(G, M ? M * kLaneElems : 2);
     const uint64_t groups = n / G;
     unsigned blocks = 0;
     hipError_t e = grid_for(m, groups, &blocks);
@@ -658,7 +659,7 @@ hipError_t launch_dsr_generic(const uint8_t *codes1, const uint16_t *s1, const u
     const uint32_t G1 = (uint32_t)group1, G2 = (uint32_t)group2;
     const bool same = G1 == G2;
     const int M = G1 % kLaneElems || G2 % kLaneElems ? 0 : unit_vectors(G2);
-    const PairMap m = pair_map(G2, M ? M * kLaneElems : 2);
+    const UnitMap m = unit_map(G2, M ? M * kLaneElems : 2);
     const uint64_t groups = n / G2;
     const uint64_t per_op = n / G1;
     const GroupDiv D1 = group_div(G1, n);
