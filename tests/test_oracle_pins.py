@@ -337,6 +337,17 @@ def test_codes_take_two_binary32_roundings():
     assert list(codes1[0, 0]) == [int(v, 16) for v in fx["packed"]]
 
 
+def test_scale_is_the_binary32_quotient_of_the_range():
+    """range/Q is exactly an fp16 tie (ties to even: 0x360E); the range times the
+    binary32 reciprocal of Q lies above the tie and would store 0x360F."""
+    fx, bits, codes1, s1, z1 = _fixture_group("scale_is_a_quotient_int4_g8_f16.txt")
+    assert int(s1[0, 0, 0]) == int(fx["s_bits"][0], 16)
+    assert int(s1[0, 0, 0]) != int(fx["s_bits_if_reciprocal"][0], 16)
+    assert int(z1[0, 0, 0]) == int(fx["z_bits"][0], 16)
+    assert list(_unpack(codes1, bits)[0, 0]) == [int(v) for v in fx["codes"]]
+    assert list(codes1[0, 0]) == [int(v, 16) for v in fx["packed"]]
+
+
 def test_stage2_zero_point_below_the_minimum():
     """A stage-2 group whose minimum sum is a tie in fp16 that rounds below it: z2 lies
     under the group, the top code clamps at Q, and that element's error is a whole scale
@@ -634,6 +645,19 @@ def test_uncompressed_sum_is_rounded_exact_sum_for_two_operands():
     exact = x.astype(np.float64).sum(axis=0)
     assert np.array_equal(out, exact.astype(np.float16).view(np.uint16))
     assert np.array_equal(out, oracle.sum_uncompressed(xb[::-1].copy(), oracle.F16))
+
+
+def test_uncompressed_sum_accumulates_in_binary32_ascending():
+    """Three operands: 1 + 2^-24 ties to 1 in binary32, so the ascending sum is +0, where the
+    exact sum and the descending order both give the subnormal 2^-24."""
+    fx = _read_fixture("uncompressed_sum_r3_f16.txt")
+    x = np.stack([_f16([float(v) for v in fx[k]]) for k in ("x0", "x1", "x2")]).reshape(3, 1, 2)
+    assert int(x[1, 0, 0]) == 0x0001
+    out = oracle.sum_uncompressed(x, oracle.F16)
+    hexes = lambda k: [int(v, 16) for v in fx[k]]
+    assert list(out[0]) == hexes("out_bits")
+    assert list(out[0]) != hexes("out_bits_if_exact")
+    assert list(out[0]) != hexes("out_bits_if_descending")
 
 
 def test_uncompressed_sum_error_bound():
