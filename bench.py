@@ -26,9 +26,11 @@ Order of a run:
      same stream: per-kernel times and K1's roofline (K1 moves two thirds of
      the bytes);
   4. the same K steps after an idle second (the cold-start figure);
-  5. the other workloads (LLaMA-3-8B prefill, the group-size sweep with its
-     errors, decode latency, tiny), the streaming ceilings, the uncompressed
-     comparator, the residual-add and linear-layer fusions, the CPU oracle.
+  5. the streaming ceilings (always), then the other workloads (LLaMA-3-8B
+     prefill, the group-size sweep with its errors, a group length that is not
+     a power of two, decode and tiny latency back to back, in a HIP graph and
+     from cold caches), the uncompressed comparator, the residual-add and
+     linear-layer fusions, the CPU oracle.
 Prints one JSON line.
 """
 from __future__ import annotations
