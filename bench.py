@@ -593,6 +593,73 @@ def clock_trace(torch, fc, step, stream, dev, name: str, blocks: int = 80, per_b
     return 0
 
 
+def stage_clocks(torch, fc, step, kernel, stream, dev, name: str, n: int = 300,
+                 iters: int = 500) -> None:
+    """At the steady clock: n pipeline steps (buffer sets in turn, as timed) with the engine
+    clock read by fc_internal_clock_probe (a one-wave kernel, ~1.5 us) before each stage
+    kernel and after the last one, and HIP events around each kernel (not the probes); then
+    each kernel back to back, n / 3 calls on the same buffer sets in turn. Prints one JSON
+    line: median and p10 MHz at the four points, median microseconds per kernel."""
+    L = fc.lib()
+    probe = L.fc_internal_clock_probe
+    probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    probe.restype = ctypes.c_int
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    buf = torch.zeros((n, 4, 4), dtype=torch.int64, device=dev)
+    it = [0]
+
+    def one_step():
+        it[0] += 1
+        step(it[0])
+
+    settle_clock(torch, one_step, stream)
+
+    def read_clock(i, j):
+        if probe(ctypes.c_void_p(buf[i, j].data_ptr()), iters, sp) != 0:
+            raise RuntimeError("fc_internal_clock_probe failed")
+
+    ev = [_events(torch, 6) for _ in range(n)]
+    for i in range(n):
+        for j in range(3):
+            read_clock(i, j)
+            ev[i][2 * j].record(stream)
+            kernel(i, j)
+            ev[i][2 * j + 1].record(stream)
+        read_clock(i, 3)
+    torch.cuda.synchronize()
+    c = buf.cpu().double()
+    mhz = (c[:, :, 0] / c[:, :, 1] * 100.0).tolist()
+    us = [[ev[i][2 * j].elapsed_time(ev[i][2 * j + 1]) * 1e3 for j in range(3)] for i in range(n)]
+
+    def med(v):
+        v = sorted(v)
+        return v[len(v) // 2]
+
+    def p10(v):
+        v = sorted(v)
+        return v[len(v) // 10]
+
+    b2b = []
+    for j in range(3):
+        def one(j=j):
+            it[0] += 1
+            kernel(it[0], j)
+
+        for _ in range(10):
+            one()
+        b2b.append(timed_calls(torch, one, stream, n // 3) * 1e3)
+    points = ["before K1", "before K2", "before K3", "after K3"]
+    print(json.dumps({"stage_clocks": {
+        "workload": name, "steps": n, "probe_fma_iterations": iters,
+        "mhz_median": {p: round(med([m[j] for m in mhz])) for j, p in enumerate(points)},
+        "mhz_p10": {p: round(p10([m[j] for m in mhz])) for j, p in enumerate(points)},
+        "us_median_in_pipeline": {k: round(med([u[j] for u in us]), 2)
+                                  for j, k in enumerate(("K1", "K2", "K3"))},
+        "us_back_to_back_sets_in_turn": {k: round(b2b[j], 2) for j, k in enumerate(("K1", "K2", "K3"))},
+        "note": "pipeline kernels bracketed by HIP events with a clock probe before each; back "
+                "to back: one kernel repeated on the buffer sets in turn"}}))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -610,7 +677,9 @@ def main() -> int:
     ap.add_argument("--clock-trace", action="store_true",
                     help="instead of the benchmark: from an idle GPU, run the pipeline in blocks "
                          "of 10 steps with the engine clock read after each block (the load-onset "
-                         "clock dip the settle phase waits out)")
+                         "clock dip the settle phase waits out); then, at the steady clock, the "
+                         "clock at each stage boundary and each kernel's time in and out of the "
+                         "pipeline")
     ap.add_argument("--quality", action="store_true",
                     help="instead of the benchmark: error (MSE) of both stages and throughput for "
                          "every block size and width of the sweep and for the five workloads")
@@ -660,22 +729,28 @@ def main() -> int:
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
-    def step(i: int, ev=None) -> None:
+    def kernel(i: int, j: int) -> None:
+        """Kernel j (0: K1, 1: K2, 2: K3) of step i."""
         xd, c1, s1, z1, c2, s2, z2, out = sets[i % 2]
-        if ev is not None:
-            ev[0].record(stream)
-        fc.fc_quantize_groups(xd, bits, group, c1, s1, z1, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        fc.fc_dequant_sum_requant(c1, s1, z1, R, T, H, bits, group, c2, s2, z2, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
-        fc.fc_dequantize(c2, s2, z2, T, H, bits, g2, tdt, out, stream=stream)
+        if j == 0:
+            fc.fc_quantize_groups(xd, bits, group, c1, s1, z1, stream=stream)
+        elif j == 1:
+            fc.fc_dequant_sum_requant(c1, s1, z1, R, T, H, bits, group, c2, s2, z2, stream=stream)
+        else:
+            fc.fc_dequantize(c2, s2, z2, T, H, bits, g2, tdt, out, stream=stream)
+
+    def step(i: int, ev=None) -> None:
+        for j in range(3):
+            if ev is not None:
+                ev[j].record(stream)
+            kernel(i, j)
         if ev is not None:
             ev[3].record(stream)
 
     if args.clock_trace:
-        return clock_trace(torch, fc, step, stream, dev, w.name)
+        rc = clock_trace(torch, fc, step, stream, dev, w.name)
+        stage_clocks(torch, fc, step, kernel, stream, dev, w.name)
+        return rc
 
     counter = [0]
 
