@@ -135,3 +135,63 @@ def test_two_streams_at_once():
         assert torch.equal(outs[i], alone[i][0]), f"stream {i}: output"
         for a, b in zip(payloads(wss[i], i), payloads(alone[i][1], i)):
             assert torch.equal(a, b), f"stream {i}: payload"
+
+
+def test_host_threads_at_once():
+    """Four host threads, each on its own stream, calling the library together (the
+    binding releases the interpreter lock during each call): the per-device caches the
+    library keeps (compute units, its allocation-free scratch address) are filled by
+    whichever call comes first, and every call gives the bits it gives alone. The
+    calls cover the three launches, the single launch, the linear layer and the
+    generic kernels; the allocation-free entry point runs on one thread only, since
+    overlapping calls of it on one device share its scratch."""
+    import threading
+
+    cases = [
+        ("steps", (4, 2048, 4096, 128, 4, synth.BF16)),
+        ("single", (8, 64, 8192, 128, 4, synth.BF16)),
+        ("generic", (4, 512, 5120, 160, 4, synth.F16)),
+        ("noalloc", (2, 256, 2048, 64, 8, synth.F16)),
+    ]
+    work = []
+    for name, (R, T, H, g, b, dt) in cases:
+        w = synth.workload("tiny").with_(name="threads", R=R, T=T, H=H, bits=b, group=g, dtype=dt)
+        xd = _dev(synth.operands(w, H + T), dt)
+        want, _ = fc.fc_allreduce_emulated(xd, b, g)
+        work.append((name, xd, b, g, want))
+    # the linear layer too, with its own compute-unit lookup
+    rng = np.random.default_rng(31)
+    la = synth.operands_from_values(rng.normal(size=(2, 300, 512)), synth.BF16)
+    lw = synth.operands_from_values(rng.normal(size=(2, 1024, 512)) * 0.05, synth.BF16)
+    la_d, lw_d = _dev(la, synth.BF16), _dev(lw, synth.BF16)
+    lin_want = fc.fc_linear_quantize(la_d, lw_d, 4, 128)
+    torch.cuda.synchronize()
+    errors = []
+
+    def run(i):
+        try:
+            s = torch.cuda.Stream()
+            name, xd, b, g, want = work[i]
+            with torch.cuda.stream(s):
+                for _ in range(8):
+                    if name == "noalloc":
+                        out = fc.fc_allreduce_emulated_noalloc(xd, b, g)
+                    else:
+                        out, _ = fc.fc_allreduce_emulated(xd, b, g)
+                    lin = fc.fc_linear_quantize(la_d, lw_d, 4, 128)
+            s.synchronize()
+            if not torch.equal(out, want):
+                errors.append(f"{name}: output")
+            for a, c in zip(lin, lin_want):
+                if a is not None and not torch.equal(a, c):
+                    errors.append(f"{name}: linear payload")
+        except Exception as e:   # reported below, from the main thread
+            errors.append(f"{work[i][0]}: {e!r}")
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(len(work))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a thread did not finish"
+    assert not errors, errors
