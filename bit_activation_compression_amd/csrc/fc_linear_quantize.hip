@@ -41,7 +41,13 @@
 //     2 XCDs and a W tile by 4 at about the same time, one of them from HBM
 //     and the others from the Infinity Cache. For short rows each XCD takes
 //     its own contiguous run of tiles. A tile's stores drain during the next
-//     tile.
+//     tile;
+//   - for long rows, each workgroup also fetches into L2, kPfDist pairs ahead
+//     of its staging, its share of the lines that the tiles running beside
+//     it on the same XCD will stage (a dword load per 128-byte line, landing
+//     in a 256-byte LDS sink): the staging loads then hit L2 instead of
+//     waiting on the Infinity Cache or HBM, which the workgroup barrier of
+//     every pair would otherwise wait for.
 #include <atomic>
 #include <type_traits>
 
@@ -70,7 +76,8 @@ constexpr int kPair = (kTileN + kTileT) * kPairK;    // 16-bit elements per pair
 constexpr int kGroupT = 4;                  // token tiles per scheduling group
 constexpr int kXcds = 8;
 constexpr int kGridT = 4;                   // XCD grid: token groups (x channel groups kXcds / kGridT)
-constexpr int kGridMinK = 3072;             // XCD-grid tile order from this K on
+constexpr int kGridMinK = 3072;             // XCD-grid tile order and L2 prefetch from this K on
+constexpr int kPfDist = 2;                  // L2 prefetch distance, in pairs beyond the newest staged
 constexpr int kLdsBytes = 160 * 1024;       // LDS per workgroup on gfx950
 // buffer resource word 3 for raw (untyped, unswizzled) 32-bit-addressed
 // buffers on gfx9-family GPUs
@@ -169,13 +176,14 @@ __device__ __forceinline__ void pair_minmax(float &mn, float &mx) {
                          __builtin_bit_cast(float, (uint32_t)b[1]));
 }
 
-template <int DT, int BITS, int G>
+template <int DT, int BITS, int G, int PFD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void linear_quantize_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, int T, int K, int H,
     int tiles_t, int tiles_n, int total, int grid, int xcd_grid, uint8_t *__restrict__ codes,
     uint16_t *__restrict__ s, uint16_t *__restrict__ z, uint16_t *__restrict__ y) {
     static_assert(G >= 8 && G <= kTileN && (G & (G - 1)) == 0, "group of 8..256 channels");
+    constexpr bool kPf = PFD > 0;               // L2 prefetch PFD pairs ahead
     // a group of 256 channels is a whole tile row: the two waves that share
     // its tokens (wn = 0, 1) each hold half of it and swap their halves'
     // minimum and maximum through LDS
@@ -196,7 +204,9 @@ void linear_quantize_kernel(
     // min/max swap area of split groups: per wave and token block, 32 (min, max) pairs
     constexpr int kXchgOff = (kStagingOff + kStagingBytes + 15) / 16 * 16;
     constexpr int kXchgBytes = kSplitGroup ? kThreads / kWave * kBlkT * 32 * 8 : 0;
-    constexpr int kLdsUsed = kXchgOff + kXchgBytes > kRingBytes ? kXchgOff + kXchgBytes : kRingBytes;
+    constexpr int kLdsData = kXchgOff + kXchgBytes > kRingBytes ? kXchgOff + kXchgBytes : kRingBytes;
+    constexpr int kSinkOff = kLdsData;          // where the prefetch loads land (never read)
+    constexpr int kLdsUsed = kLdsData + (kPf ? 256 : 0);
     static_assert(kLdsUsed <= kLdsBytes && kStagingBytes + kXchgBytes <= kRingBytes,
                   "staging fits in LDS");
     __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsUsed / 2];
@@ -223,6 +233,12 @@ void linear_quantize_kernel(
         int r, n0, t0;
         uint32_t abytes;                 // bytes of the tile's real token rows of A
         const uint16_t *wb, *ab;         // the tile's first W and A rows
+        // L2 prefetch share: this tile's W tile is staged by the w_share
+        // tiles of its scheduling group with the same channels (token index
+        // pf_t among them), its A tile by the a_share with the same tokens
+        // (channel index pf_n); each fetches 1/w_share of the W rows and
+        // 1/a_share of the A rows (log2 of the shares; -1: fetch nothing)
+        int pf_t, pf_n, w_log, a_log;
     };
     // Tile of iteration `it` of this workgroup; false when there is none.
     // The A resource covers only the tile's real token rows: rows past T read
@@ -269,6 +285,13 @@ void linear_quantize_kernel(
         tl.abytes = (uint32_t)min(kTileT, T - tl.t0) * rowb;
         tl.wb = Wb;
         tl.ab = Ab;
+        // the XCD's 32 workgroups run 4 token x 8 channel tiles of a group
+        // at a time (fewer channel tiles when the group is narrower)
+        const int a_share = span_n >= 8 ? 8 : span_n >= 4 ? 4 : span_n >= 2 ? 2 : 1;
+        tl.pf_t = in_grp % gsize;
+        tl.pf_n = (in_grp / gsize) % a_share;
+        tl.w_log = gsize == 4 ? 2 : gsize == 2 ? 1 : gsize == 1 ? 0 : -1;
+        tl.a_log = a_share == 8 ? 3 : a_share == 4 ? 2 : a_share == 2 ? 1 : 0;
         return true;
     };
 
@@ -340,6 +363,28 @@ void linear_quantize_kernel(
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) pair_in_part(lo, tl, p, nb);
     };
+    // L2 prefetch of this workgroup's share of pair p: one dword per 128-byte
+    // staged line (row r of a tile: bytes r * rowb + 128 p). Waves 0..3 take
+    // the W rows of the share (64 >> w_log each), waves 4..7 the A rows (64
+    // >> a_log each). One instruction per wave whatever the share, so that
+    // the wait counts stay fixed: lanes with no line, and pairs past the last,
+    // read past the end of the resource (no memory access; zeros land in the
+    // sink). Rows past T lie past the A resource too.
+    auto prefetch = [&](const Tile &tl, int p) {
+        const uint32_t l = fresh((uint32_t)lane);
+        const bool on_w = wave < 4;
+        const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(on_w ? tl.wb : tl.ab), (short)0,
+            (int)(on_w ? kTileN * rowb : tl.abytes), kRawBufferFlags);
+        const int lg = on_w ? tl.w_log : tl.a_log;
+        const uint32_t per_wave = lg >= 0 ? 64u >> lg : 0u;          // rows per wave
+        const uint32_t first = (uint32_t)(on_w ? tl.pf_t : tl.pf_n) * per_wave * 4u +
+                               (uint32_t)(wave & 3) * per_wave;
+        const bool live = l < per_wave && p < KP;
+        const uint32_t off = live ? (first + l) * rowb + (uint32_t)p * (kPairK * 2) : 0xFFFFFFF0u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            res, (__attribute__((address_space(3))) void *)(lds + kSinkOff / 2), 4, off, 0, 0, 0);
+    };
 
     // fragment reads: row (block base + lane % 32), chunk 4 h + 2 ks + lane / 32
     // for step ks of stage kt = 2 p + h (half h of pair p). The rotation of a
@@ -389,10 +434,12 @@ void linear_quantize_kernel(
         // pair p + 1 and the issue of half of pair p + 2 into pair p's buffer,
         // the step after it the other half (two bursts of staging requests
         // instead of one: measured 1-3% faster; not for 4-bit codes in groups
-        // of 8, which would then run out of registers). Nothing else is
-        // outstanding at that wait, so it is vmcnt(0). (Loads complete in
-        // order, so these counts hold with the previous tile's stores still in
-        // flight too.)
+        // of 8, which would then run out of registers). With the L2 prefetch,
+        // the step after that issues the prefetch of pair p + 2 + PFD, the one
+        // load that stays in flight across the wait (vmcnt(1)); otherwise
+        // nothing else is outstanding there, and the wait is vmcnt(0). (Loads
+        // complete in order, so these counts hold with the previous tile's
+        // stores still in flight too.)
         // The wait, the barrier and the issue sit behind uniform branches; the
         // matrix-core work is never under a condition, which would make the
         // compiler spill the accumulators.
@@ -428,12 +475,17 @@ void linear_quantize_kernel(
             });
             const bool odd = (kt & 1) != 0;
             if (odd) {
-                wait_loads<0>();
+                if constexpr (kPf) wait_loads<1>();   // all but the prefetch of stage kt - 1
+                else wait_loads<0>();
                 barrier_keep_loads();
             }
             const bool issue = odd && (kt >> 1) + 2 < KP;
             step(1, [&](int nb) {
                 frag_part(lo, kt + 1, 0, nb, fw[0], fa[0]);
+                if constexpr (kPf) {
+                    // every even stage but the last, after its staging loads
+                    if (!odd && nb == 0) prefetch(cur, (kt >> 1) + 1 + PFD);
+                }
                 if constexpr (kSplitIssue) {
                     if (issue && (nb & 1)) pair_in_part(lo, cur, (kt >> 1) + 2, nb >> 1);
                 } else {
@@ -613,7 +665,10 @@ int compute_units() {
 // K >= kGridMinK (measured on the 70B layer shapes, K = 2048 ... 7168: the
 // grid is 2-5% faster from K = 3072 on, where the shared reads come from the
 // Infinity Cache; at K = 2048 the XCD runs are 2% faster). The grid needs the
-// XCD split of the tiles, tiles_t % 4 == 0 and tiles_n % 2 == 0.
+// XCD split of the tiles, tiles_t % 4 == 0 and tiles_n % 2 == 0. The L2
+// prefetch runs from K = kGridMinK on, in either order (measured on the 70B
+// and 8B layer shapes: 3-6% faster at K = 3584 and 7168; at K = 1024 and
+// 2048, where the operands nearly fit the Infinity Cache, 0.5-2% slower).
 template <int DT, int BITS, int G>
 hipError_t launch_one(const uint16_t *a, const uint16_t *w, int R, int T, int K, int H,
                       uint8_t *codes, uint16_t *s, uint16_t *z, uint16_t *y, hipStream_t stream,
@@ -628,9 +683,14 @@ hipError_t launch_one(const uint16_t *a, const uint16_t *w, int R, int T, int K,
     const bool can_grid = total % kXcds == 0 && grid % kXcds == 0 && tiles_t % kGridT == 0 &&
                           tiles_n % (kXcds / kGridT) == 0;
     const int xcd_grid = can_grid && (order < 0 ? K >= kGridMinK : order != 0);
-    hipLaunchKernelGGL((linear_quantize_kernel<DT, BITS, G>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, stream, a, w, T, K, H, tiles_t, tiles_n, (int)total,
-                       grid, xcd_grid, codes, s, z, y);
+    if (K >= kGridMinK)
+        hipLaunchKernelGGL((linear_quantize_kernel<DT, BITS, G, kPfDist>), dim3((unsigned)grid),
+                           dim3(kThreads), 0, stream, a, w, T, K, H, tiles_t, tiles_n, (int)total,
+                           grid, xcd_grid, codes, s, z, y);
+    else
+        hipLaunchKernelGGL((linear_quantize_kernel<DT, BITS, G, 0>), dim3((unsigned)grid),
+                           dim3(kThreads), 0, stream, a, w, T, K, H, tiles_t, tiles_n, (int)total,
+                           grid, xcd_grid, codes, s, z, y);
     return hipGetLastError();
 }
 

@@ -96,6 +96,10 @@ EXACT = [  # (R, T, K, H, group, bits, dtype)
     (2, 300, 160, 512, 256, 4, oracle.BF16),    # groups of 256: a tile row, split over two waves
     (1, 257, 64, 256, 256, 8, oracle.F16),      # the same, one channel tile, INT8
     (2, 2048, 3072, 512, 256, 4, oracle.F16),   # the same on the XCD grid
+    # long rows (K >= 3072) also prefetch into L2
+    (1, 300, 3104, 256, 8, 4, oracle.BF16),     # 4-bit codes in groups of 8, odd stage count
+    (2, 1792, 3072, 512, 128, 4, oracle.F16),   # 7 token tiles: scheduling groups of 4 and 3
+    (1, 512, 3072, 512, 16, 8, oracle.BF16),    # INT8 in groups of 16 (the largest LDS use)
 ]
 
 
