@@ -257,6 +257,8 @@ def fc_linear_quantize(a: torch.Tensor, w: torch.Tensor, bits: int, group: int, 
     R, T, K = a.shape
     H = w.shape[1]
     dev = a.device
+    if w.device != dev:
+        raise ValueError(f"w is on {w.device}, a on {dev}")
     if codes1 is None:
         codes1 = torch.empty((R, T, H * bits // 8), dtype=torch.uint8, device=dev)
     if s1 is None:
@@ -320,7 +322,7 @@ def fc_allreduce_emulated(x: torch.Tensor, bits: int, group: int, out=None, work
     _room(workspace, "workspace", 0, dev)
     ws_bytes = workspace.numel() * workspace.element_size()
     if residual is not None:
-        _dev_tensor(residual, "residual")
+        _room(residual, "residual", T * H * 2, dev)
         if residual.dtype != x.dtype or tuple(residual.shape) != (T, H):
             raise ValueError("residual must be [T, H] of x's dtype")
         st = lib().fc_allreduce_emulated_residual(_ptr(x), _dt(x, "x"), R, T, H, bits, bits2,

@@ -63,6 +63,15 @@ def test_layout_dtype_and_device_are_checked():
                                                              device="cuda"))
     with pytest.raises(ValueError, match="GPU tensor"):
         fc.fc_sum_uncompressed(x, out=torch.empty((8, 256), dtype=x.dtype))
+    # the residual is a caller buffer like the others, and it must be [T, H]
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fc.fc_allreduce_emulated(x, 4, 128, residual=torch.empty((8, 256), dtype=x.dtype))
+    with pytest.raises(ValueError, match="residual holds"):
+        fc.fc_allreduce_emulated(x, 4, 128, residual=torch.empty((8, 255), dtype=x.dtype,
+                                                                  device="cuda"))
+    with pytest.raises(ValueError, match=r"residual must be \[T, H\]"):
+        fc.fc_allreduce_emulated(x, 4, 128, residual=torch.empty((4, 512), dtype=x.dtype,
+                                                                  device="cuda"))
     # the layer output must have the operands' dtype (a float32 buffer of the same
     # byte count would otherwise receive 16-bit values)
     a = _x(2, 8, 64)
