@@ -211,7 +211,30 @@ __device__ __forceinline__ void sum_pair(const uint8_t *codes1, const uint16_t *
                                          const uint16_t *z1, int R, uint64_t n, uint64_t per_op,
                                          const GroupDiv &D1, uint64_t e, float &ya, float &yb) {
     const uint64_t g = group_of(e, D1);
-    for (int r = 0; r < R; ++r) {
+    // operands in pairs: both operands' codes, scales and zeros are loaded
+    // before the first of their terms is added; an odd last one goes alone
+    int r = 0;
+    for (; r + 2 <= R; r += 2) {
+        float qa[2], qb[2];
+        uint16_t sv[2], zv[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            load_pair_codes<BITS1>(codes1, (uint64_t)(r + i) * n + e, qa[i], qb[i]);
+            const uint64_t mi = (uint64_t)(r + i) * per_op + g;
+            sv[i] = s1[mi];
+            zv[i] = z1[mi];
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float s = half_bits_to_float(sv[i]);
+            const float z = half_bits_to_float(zv[i]);
+            const float xa = __builtin_fmaf(qa[i], s, z);
+            const float xb = __builtin_fmaf(qb[i], s, z);
+            ya = r + i == 0 ? xa : ya + xa;
+            yb = r + i == 0 ? xb : yb + xb;
+        }
+    }
+    for (; r < R; ++r) {
         float qa, qb;
         load_pair_codes<BITS1>(codes1, (uint64_t)r * n + e, qa, qb);
         const uint64_t mi = (uint64_t)r * per_op + g;
