@@ -110,6 +110,12 @@ CASES = [  # R, T, H, bits1, bits2, group, dtype
     (16, 4, 1536, 4, 4, 96, synth.F16),      # R = 16: the reduction's run-time operand loop
     (24, 3, 2304, 8, 4, 96, synth.BF16),     # R = 24, mixed widths
     (12, 5, 1440, 4, 4, 120, synth.F16),     # R = 12, units of 1 vector (15 of 16 lanes)
+    # groups of at most 32 values, not a multiple of 8: a lane owns a group in stage 1
+    (4, 37, 1280, 4, 4, 10, synth.F16),      # 296 full waves of groups
+    (3, 13, 420, 8, 8, 14, synth.BF16),      # INT8, a partial last wave
+    (2, 9, 960, 4, 8, 30, synth.F16),        # the longest such group, mixed widths
+    (5, 3, 3200, 8, 4, 10, synth.BF16),      # R = 5
+    (4, 6, 2080, 4, 4, 26, synth.F16),       # 13 pairs per lane
 ]
 
 
