@@ -353,6 +353,54 @@ __global__ __launch_bounds__(kBlockThreads) void dsr_generic_kernel(
     }
 }
 
+// Equal group lengths of at most kLaneGroupMax that are not a multiple of 8:
+// a lane owns a stage-2 group (which is also one stage-1 group of every
+// operand). Its sums stay in registers (pair slots up to kLaneGroupMax / 2,
+// guarded by the group's pair count), summed in ascending r as in sum_pair.
+template <int BITS1, int BITS2>
+__global__ __launch_bounds__(kBlockThreads) void dsr_lane_kernel(
+    const uint8_t *__restrict__ codes1, const uint16_t *__restrict__ s1,
+    const uint16_t *__restrict__ z1, int R, uint64_t n, uint64_t per_op, uint64_t groups,
+    uint32_t G, uint8_t *__restrict__ codes2, uint16_t *__restrict__ s2,
+    uint16_t *__restrict__ z2) {
+    constexpr uint32_t kMaxPairs = kLaneGroupMax / 2;
+    const uint64_t g = wave_index() * kWave + (uint32_t)lane_id();
+    if (g >= groups) return;
+    const uint32_t pairs = G / 2;
+    const uint64_t e0 = g * G;
+    float ya[kMaxPairs], yb[kMaxPairs];
+    for (int r = 0; r < R; ++r) {
+        const uint64_t mi = (uint64_t)r * per_op + g;
+        const float s = half_bits_to_float(s1[mi]);
+        const float z = half_bits_to_float(z1[mi]);
+#pragma unroll
+        for (uint32_t j = 0; j < kMaxPairs; ++j) {
+            if (j < pairs) {
+                float qa, qb;
+                load_pair_codes<BITS1>(codes1, (uint64_t)r * n + e0 + 2 * j, qa, qb);
+                const float xa = __builtin_fmaf(qa, s, z);
+                const float xb = __builtin_fmaf(qb, s, z);
+                ya[j] = r == 0 ? xa : ya[j] + xa;
+                yb[j] = r == 0 ? xb : yb[j] + xb;
+            }
+        }
+    }
+    float mn = kInf, mx = -kInf;
+#pragma unroll
+    for (uint32_t j = 0; j < kMaxPairs; ++j) {
+        if (j < pairs) {
+            mn = __builtin_fminf(mn, __builtin_fminf(ya[j], yb[j]));
+            mx = __builtin_fmaxf(mx, __builtin_fmaxf(ya[j], yb[j]));
+        }
+    }
+    const GroupParams p = group_params<BITS2>(mn, mx);
+#pragma unroll
+    for (uint32_t j = 0; j < kMaxPairs; ++j)
+        if (j < pairs) store_pair_codes<BITS2>(codes2, e0 + 2 * j, encode2<BITS2>(ya[j], yb[j], p));
+    s2[g] = p.s16;
+    z2[g] = p.z16;
+}
+
 // ---------------------------------------------------------------------------
 // final dequantize (+ residual add): one pair of positions per lane; D2
 // divides by G2
@@ -800,6 +848,22 @@ hipError_t launch_dsr_generic(const uint8_t *codes1, const uint16_t *s1, const u
     const uint64_t groups = n / G2;
     const uint64_t per_op = n / G1;
     const GroupDiv D1 = group_div(G1, n);
+    if (M == 0 && same && G2 <= kLaneGroupMax) {
+        const uint64_t b = (groups + (uint64_t)kWave * kWavesPerBlock - 1) / ((uint64_t)kWave * kWavesPerBlock);
+        if (b > 0x7FFFFFFFull || b == 0) return hipErrorInvalidConfiguration;
+#define FC_LANE(B1, B2)                                                                                \
+    hipLaunchKernelGGL((dsr_lane_kernel<B1, B2>), dim3((unsigned)b), dim3(kBlockThreads), 0, stream, \
+                       codes1, s1, z1, R, n, per_op, groups, G2, codes2, s2, z2)
+        if (bits1 == 4) {
+            if (bits2 == 4) FC_LANE(4, 4);
+            else FC_LANE(4, 8);
+        } else {
+            if (bits2 == 4) FC_LANE(8, 4);
+            else FC_LANE(8, 8);
+        }
+#undef FC_LANE
+        return hipGetLastError();
+    }
     unsigned blocks = 0;
     hipError_t e = grid_for(m, groups, &blocks);
     if (e != hipSuccess) return e;
